@@ -1,0 +1,222 @@
+"""MI355X (gfx950) GQA attention backward: thin Python binding of the C ABI.
+
+The functions here carry the names of the C entry points declared in
+``include/attn_bwd.h`` and only marshal arguments: they check tensor
+dtypes/shapes/devices, pass raw device pointers and the current HIP stream,
+and raise :class:`AttnError` on a non-zero status.  All computation happens in
+the HIP kernels of ``libattn_bwd.so``; there is no CPU fallback.  If the
+library has not been built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "AttnError",
+    "Shape",
+    "lib",
+    "attn_fwd",
+    "attn_bwd_preprocess",
+    "attn_bwd",
+    "attn_bwd_postprocess",
+    "attn_abi_version",
+    "LIB_PATH",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn_bwd.so")
+
+ATTN_F16, ATTN_BF16 = 0, 1
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_HIP"}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    """Mirror of ``attn_shape_t``."""
+
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("max_seqlen", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int32),
+        ("hq", ctypes.c_int32),
+        ("hkv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+    @classmethod
+    def make(cls, *, num_seqs, max_seqlen, total_tokens, hq, hkv, head_dim, causal, window,
+             scale, dtype) -> "Shape":
+        if not isinstance(dtype, int):
+            dtype = _dtype_code(dtype)
+        return cls(int(num_seqs), int(max_seqlen), int(total_tokens), int(hq), int(hkv),
+                   int(head_dim), int(bool(causal)), int(window), float(scale), int(dtype))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libattn_bwd.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m atomics_bwd_preprocess_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S = ctypes.c_void_p, ctypes.POINTER(Shape)
+        sig = {
+            "attn_fwd": [S, P, P, P, P, P, P, P, P],
+            "attn_bwd_preprocess": [S, P, P, P, P, P, P, P, P, P],
+            "attn_bwd": [S, P, P, P, P, P, P, P, P, P, P, P],
+            "attn_bwd_postprocess": [S, P, P, P],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.attn_status_string.argtypes = [ctypes.c_int]
+        L.attn_status_string.restype = ctypes.c_char_p
+        L.attn_last_error.argtypes = []
+        L.attn_last_error.restype = ctypes.c_char_p
+        L.attn_abi_version.argtypes = []
+        L.attn_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def attn_abi_version() -> int:
+    return lib().attn_abi_version()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise AttnError(status, lib().attn_last_error().decode())
+
+
+def _dtype_code(dt) -> int:
+    import torch
+
+    if dt in (torch.float16, "f16", "fp16"):
+        return ATTN_F16
+    if dt in (torch.bfloat16, "bf16"):
+        return ATTN_BF16
+    raise AttnError(2, f"unsupported dtype {dt}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t, name, dtype, shape, allow_none=False):
+    import torch
+
+    if t is None:
+        if allow_none:
+            return
+        raise AttnError(1, f"{name} is required")
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise AttnError(1, f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise AttnError(1, f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise AttnError(1, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise AttnError(1, f"{name} must be contiguous")
+
+
+def _dims(shape: Shape):
+    import torch
+
+    T, Hq, Hkv, D = shape.total_tokens, shape.hq, shape.hkv, shape.head_dim
+    dt = torch.float16 if shape.dtype == ATTN_F16 else torch.bfloat16
+    return T, Hq, Hkv, D, dt
+
+
+def _cu(shape: Shape, cu_seqlens):
+    import torch
+
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (shape.num_seqs + 1,))
+    return _ptr(cu_seqlens)
+
+
+def attn_fwd(shape: Shape, q, k, v, cu_seqlens, sink, o, lse, stream=None) -> None:
+    """Forward: writes ``o`` [T,Hq,D] and ``lse`` [Hq,T] (fp32)."""
+    import torch
+
+    T, Hq, Hkv, D, dt = _dims(shape)
+    _need(q, "q", dt, (T, Hq, D))
+    _need(k, "k", dt, (T, Hkv, D))
+    _need(v, "v", dt, (T, Hkv, D))
+    _need(sink, "sink", torch.float32, (Hq,), allow_none=True)
+    _need(o, "o", dt, (T, Hq, D))
+    _need(lse, "lse", torch.float32, (Hq, T))
+    _check(lib().attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _cu(shape, cu_seqlens),
+                          _ptr(sink), _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def attn_bwd_preprocess(shape: Shape, o, dout, lse, cu_seqlens, sink, delta, dq_accum, dsink,
+                        stream=None) -> None:
+    """Delta = rowsum(O * dO) [Hq,T]; dq_accum := 0; dsink [Hq] if a sink is given."""
+    import torch
+
+    T, Hq, Hkv, D, dt = _dims(shape)
+    _need(o, "o", dt, (T, Hq, D))
+    _need(dout, "dout", dt, (T, Hq, D))
+    _need(lse, "lse", torch.float32, (Hq, T), allow_none=sink is None)
+    _need(sink, "sink", torch.float32, (Hq,), allow_none=True)
+    _need(delta, "delta", torch.float32, (Hq, T))
+    _need(dq_accum, "dq_accum", torch.float32, (T, Hq, D))
+    _need(dsink, "dsink", torch.float32, (Hq,), allow_none=True)
+    _check(lib().attn_bwd_preprocess(ctypes.byref(shape), _ptr(o), _ptr(dout), _ptr(lse),
+                                     _cu(shape, cu_seqlens), _ptr(sink), _ptr(delta),
+                                     _ptr(dq_accum), _ptr(dsink), _stream(stream)))
+
+
+def attn_bwd(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dq_accum, dk, dv,
+             stream=None) -> None:
+    """Main backward: accumulates dQ into dq_accum (atomics) and writes dk, dv."""
+    import torch
+
+    T, Hq, Hkv, D, dt = _dims(shape)
+    _need(q, "q", dt, (T, Hq, D))
+    _need(k, "k", dt, (T, Hkv, D))
+    _need(v, "v", dt, (T, Hkv, D))
+    _need(dout, "dout", dt, (T, Hq, D))
+    _need(lse, "lse", torch.float32, (Hq, T))
+    _need(delta, "delta", torch.float32, (Hq, T))
+    _need(dq_accum, "dq_accum", torch.float32, (T, Hq, D))
+    _need(dk, "dk", dt, (T, Hkv, D))
+    _need(dv, "dv", dt, (T, Hkv, D))
+    _check(lib().attn_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                          _ptr(delta), _cu(shape, cu_seqlens), _ptr(dq_accum), _ptr(dk), _ptr(dv),
+                          _stream(stream)))
+
+
+def attn_bwd_postprocess(shape: Shape, dq_accum, dq, stream=None) -> None:
+    """dq = RNE cast of the fp32 dq_accum."""
+    import torch
+
+    T, Hq, Hkv, D, dt = _dims(shape)
+    _need(dq_accum, "dq_accum", torch.float32, (T, Hq, D))
+    _need(dq, "dq", dt, (T, Hq, D))
+    _check(lib().attn_bwd_postprocess(ctypes.byref(shape), _ptr(dq_accum), _ptr(dq),
+                                      _stream(stream)))

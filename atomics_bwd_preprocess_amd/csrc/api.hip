@@ -1,0 +1,183 @@
+// C ABI of the attention backward library: argument validation, then one or
+// two kernel launches on the caller's stream.  No allocation, no state, no
+// synchronisation.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdint.h>
+
+#include "../../include/attn_bwd.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+attn_status_t fail(attn_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+attn_status_t ok() {
+  g_last_error[0] = '\0';
+  return ATTN_OK;
+}
+
+attn_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQUIRE(cond, ...)                                   \
+  do {                                                       \
+    if (!(cond)) return fail(ATTN_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_TENSOR(ptr)                                                        \
+  do {                                                                             \
+    REQUIRE((ptr) != nullptr, "%s is NULL", #ptr);                                 \
+    REQUIRE(aligned((ptr), 16), "%s is not 16-byte aligned", #ptr);                \
+  } while (0)
+
+#define REQUIRE_F32(ptr)                                                           \
+  do {                                                                             \
+    REQUIRE((ptr) != nullptr, "%s is NULL", #ptr);                                 \
+    REQUIRE(aligned((ptr), 4), "%s is not 4-byte aligned", #ptr);                  \
+  } while (0)
+
+// Validates the problem description; fills `p`.
+attn_status_t check_shape(const attn_shape_t* s, const int32_t* cu, bool need_cu_check,
+                          attn::Problem& p) {
+  REQUIRE(s != nullptr, "shape is NULL");
+  REQUIRE(s->num_seqs >= 1, "num_seqs must be >= 1 (got %d)", s->num_seqs);
+  REQUIRE(s->max_seqlen >= 1, "max_seqlen must be >= 1 (got %d)", s->max_seqlen);
+  REQUIRE(s->total_tokens >= 0, "total_tokens must be >= 0 (got %d)", s->total_tokens);
+  REQUIRE(s->hq >= 1 && s->hkv >= 1, "hq and hkv must be >= 1 (got %d, %d)", s->hq, s->hkv);
+  REQUIRE(s->hq % s->hkv == 0, "hq (%d) must be a multiple of hkv (%d)", s->hq, s->hkv);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", s->head_dim);
+  if (s->dtype != ATTN_F16 && s->dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", s->dtype);
+  REQUIRE(s->causal == 0 || s->causal == 1, "causal must be 0 or 1 (got %d)", s->causal);
+  REQUIRE(s->window >= 0, "window must be >= 0 (got %d)", s->window);
+  REQUIRE(s->window == 0 || s->causal, "a sliding window requires causal = 1");
+  REQUIRE(isfinite(s->scale) && s->scale > 0.0f, "scale must be finite and > 0");
+  // 64-bit element counts must fit the launch geometry and index math.
+  const long long rows = (long long)s->total_tokens * s->hq;
+  REQUIRE(rows * s->head_dim < (1LL << 40), "tensor too large");
+  const long long blocks = (long long)((s->max_seqlen + 63) / 64) * s->num_seqs * s->hq;
+  REQUIRE(blocks < (1LL << 31), "launch grid too large");
+  if (need_cu_check && cu == nullptr)
+    REQUIRE((long long)s->num_seqs * s->max_seqlen == s->total_tokens,
+            "cu_seqlens is NULL but total_tokens != num_seqs * max_seqlen");
+  if (cu != nullptr) REQUIRE(aligned(cu, 4), "cu_seqlens is not 4-byte aligned");
+  p.num_seqs = s->num_seqs;
+  p.max_seqlen = s->max_seqlen;
+  p.total = s->total_tokens;
+  p.hq = s->hq;
+  p.hkv = s->hkv;
+  p.d = s->head_dim;
+  p.causal = s->causal != 0;
+  p.window = s->window;
+  p.scale = s->scale;
+  p.bf16 = s->dtype == ATTN_BF16;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd(const attn_shape_t* shape, const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens, const float* sink, void* o, float* lse,
+                       hipStream_t stream) {
+  attn::Problem p;
+  attn_status_t st = check_shape(shape, cu_seqlens, true, p);
+  if (st != ATTN_OK) return st;
+  REQUIRE_TENSOR(q);
+  REQUIRE_TENSOR(k);
+  REQUIRE_TENSOR(v);
+  REQUIRE_TENSOR(o);
+  REQUIRE_F32(lse);
+  if (sink) REQUIRE(aligned(sink, 4), "sink is not 4-byte aligned");
+  if (p.total == 0) return ok();
+  return hip_status(attn::launch_fwd(p, q, k, v, cu_seqlens, sink, o, lse, stream), "attn_fwd");
+}
+
+attn_status_t attn_bwd_preprocess(const attn_shape_t* shape, const void* o, const void* dout,
+                                  const float* lse, const int32_t* cu_seqlens,
+                                  const float* sink, float* delta, float* dq_accum,
+                                  float* dsink, hipStream_t stream) {
+  attn::Problem p;
+  attn_status_t st = check_shape(shape, cu_seqlens, true, p);
+  if (st != ATTN_OK) return st;
+  REQUIRE_TENSOR(o);
+  REQUIRE_TENSOR(dout);
+  REQUIRE_TENSOR(dq_accum);
+  REQUIRE_F32(delta);
+  REQUIRE((sink == nullptr) == (dsink == nullptr), "sink and dsink must both be NULL or both set");
+  if (sink) {
+    REQUIRE_F32(lse);
+    REQUIRE_F32(sink);
+    REQUIRE_F32(dsink);
+  }
+  if (p.total == 0) {
+    if (!sink) return ok();
+  }
+  return hip_status(attn::launch_preprocess(p, o, dout, lse, sink, delta, dq_accum, dsink, stream),
+                    "attn_bwd_preprocess");
+}
+
+attn_status_t attn_bwd(const attn_shape_t* shape, const void* q, const void* k, const void* v,
+                       const void* dout, const float* lse, const float* delta,
+                       const int32_t* cu_seqlens, float* dq_accum, void* dk, void* dv,
+                       hipStream_t stream) {
+  attn::Problem p;
+  attn_status_t st = check_shape(shape, cu_seqlens, true, p);
+  if (st != ATTN_OK) return st;
+  REQUIRE_TENSOR(q);
+  REQUIRE_TENSOR(k);
+  REQUIRE_TENSOR(v);
+  REQUIRE_TENSOR(dout);
+  REQUIRE_F32(lse);
+  REQUIRE_F32(delta);
+  REQUIRE_TENSOR(dq_accum);
+  REQUIRE_TENSOR(dk);
+  REQUIRE_TENSOR(dv);
+  if (p.total == 0) return ok();
+  return hip_status(attn::launch_bwd(p, q, k, v, dout, lse, delta, cu_seqlens, dq_accum, dk, dv,
+                                     stream),
+                    "attn_bwd");
+}
+
+attn_status_t attn_bwd_postprocess(const attn_shape_t* shape, const float* dq_accum, void* dq,
+                                   hipStream_t stream) {
+  attn::Problem p;
+  attn_status_t st = check_shape(shape, nullptr, false, p);
+  if (st != ATTN_OK) return st;
+  REQUIRE_TENSOR(dq_accum);
+  REQUIRE_TENSOR(dq);
+  if (p.total == 0) return ok();
+  return hip_status(attn::launch_postprocess(p, dq_accum, dq, stream), "attn_bwd_postprocess");
+}
+
+const char* attn_status_string(attn_status_t status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+}  // extern "C"

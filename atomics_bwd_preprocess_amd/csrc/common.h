@@ -1,0 +1,116 @@
+// Device helpers shared by the gfx950 attention kernels: vector types, MFMA
+// wrappers, 16-bit conversions and small wave-level primitives.
+//
+// MFMA 32x32x16 (v_mfma_f32_32x32x16_{f16,bf16}) register layout used
+// throughout (wave64, lane l, c = l / 32, n = l % 32):
+//   A (32 x 16): lane l holds row n, k-slots (c, e), e = 0..7   (8 x 16-bit)
+//   B (16 x 32): lane l holds column n, k-slots (c, e)          (8 x 16-bit)
+//   C (32 x 32): lane l, register r = 0..15 holds
+//                row (r / 4) * 8 + 4 * c + (r % 4), column n.
+// A and B pair the same slot (c, e) in the contraction, so any assignment of
+// k indices to slots is valid as long as both operands use the same one.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T> struct V8;
+template <> struct V8<_Float16> { typedef f16x8 type; typedef f16x4 half_type; };
+template <> struct V8<__bf16> { typedef bf16x8 type; typedef bf16x4 half_type; };
+
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Round-to-nearest-even conversion of fp32 to the 16-bit storage type.
+template <typename T> __device__ __forceinline__ T to16(float x) { return static_cast<T>(x); }
+
+template <typename T> __device__ __forceinline__ typename V8<T>::type zero8() {
+  typename V8<T>::type z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = static_cast<T>(0.0f);
+  return z;
+}
+
+// 16-byte and 8-byte raw moves (global or LDS, by address space inference).
+template <typename T> __device__ __forceinline__ typename V8<T>::type ld16(const T* p) {
+  return __builtin_bit_cast(typename V8<T>::type, *reinterpret_cast<const u32x4*>(p));
+}
+template <typename T> __device__ __forceinline__ void st16(T* p, typename V8<T>::type v) {
+  *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, v);
+}
+template <typename T> __device__ __forceinline__ typename V8<T>::half_type ld8(const T* p) {
+  return __builtin_bit_cast(typename V8<T>::half_type, *reinterpret_cast<const u32x2*>(p));
+}
+template <typename T> __device__ __forceinline__ void st8(T* p, typename V8<T>::half_type v) {
+  *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v);
+}
+
+// Concatenate two 4-element halves into one 8-element MFMA operand.
+template <typename T>
+__device__ __forceinline__ typename V8<T>::type cat8(typename V8<T>::half_type lo,
+                                                     typename V8<T>::half_type hi) {
+  typename V8<T>::type r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = lo[i];
+    r[i + 4] = hi[i];
+  }
+  return r;
+}
+
+// Pack registers [base, base + 8) of an MFMA C tile into an operand.
+template <typename T>
+__device__ __forceinline__ typename V8<T>::type pack8(const f32x16& v, int base) {
+  typename V8<T>::type r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = to16<T>(v[base + i]);
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by lane (l ^ 32).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Sequence bounds [a, b) clamped to [0, total]; cu == nullptr means a dense batch.
+__device__ __forceinline__ void seq_bounds(const int32_t* cu, int s, int max_seqlen, int total,
+                                           int& a, int& b) {
+  long long lo, hi;
+  if (cu) {
+    lo = cu[s];
+    hi = cu[s + 1];
+  } else {
+    lo = (long long)s * max_seqlen;
+    hi = lo + max_seqlen;
+  }
+  lo = lo < 0 ? 0 : (lo > total ? total : lo);
+  hi = hi < lo ? lo : (hi > total ? total : hi);
+  a = (int)lo;
+  b = (int)hi;
+}
+
+// Visibility of key position j to query position i (local to one sequence).
+__device__ __forceinline__ bool visible(int i, int j, bool causal, int window) {
+  return (!causal || j <= i) && (window <= 0 || j > i - window);
+}
+
+}  // namespace attn

@@ -1,0 +1,35 @@
+// Host-side launchers of the gfx950 kernels (called by the C ABI in api.hip
+// after argument validation).  Every launcher only enqueues on `stream` and
+// returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct Problem {
+  int num_seqs, max_seqlen, total, hq, hkv, d;
+  bool causal;
+  int window;
+  float scale;
+  bool bf16;
+};
+
+hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v,
+                      const int32_t* cu, const float* sink, void* o, float* lse,
+                      hipStream_t stream);
+
+hipError_t launch_preprocess(const Problem& p, const void* o, const void* dout, const float* lse,
+                             const float* sink, float* delta, float* dq_accum, float* dsink,
+                             hipStream_t stream);
+
+hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void* v,
+                      const void* dout, const float* lse, const float* delta,
+                      const int32_t* cu, float* dq_accum, void* dk, void* dv,
+                      hipStream_t stream);
+
+hipError_t launch_postprocess(const Problem& p, const float* dq_accum, void* dq,
+                              hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,135 @@
+// Backward preprocess and postprocess: the HBM-bound kernels around the main
+// backward pass.
+//
+//  * preprocess  (tilelang-ascend PR "GQA Sink Backward BHSD": the merged
+//    preprocess + dsink kernel, and Phase 0 / Phase 5 of its single backward
+//    kernel): Delta = row sum of O * dO in fp32, zeroing of the fp32 dQ
+//    accumulator, and dsink = -sum_t exp(sink - lse) * Delta.
+//  * postprocess (same PR: the postprocess kernel that casts the fp32
+//    accumulated gradient to fp16): dQ = RNE cast of the fp32 accumulator.
+//
+// Algorithmic bytes (e = 2 bytes per 16-bit element, R = T * Hq rows):
+//   delta kernel:  R * D * 2e (O, dO) + R * 4 (Delta) + R * D * 4 (zeroing)
+//   dsink kernel:  R * 8 (lse, Delta)
+//   postprocess:   R * D * (4 + e)
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+
+// One workgroup: query head blockIdx.y, tokens [blockIdx.x * 64, +64).
+// A row (token, head) is D contiguous elements read as 16-byte chunks by
+// D / 8 consecutive lanes; the partial dot products are reduced across those
+// lanes with xor shuffles (which stay inside a row group).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o,
+                                                    const T* __restrict__ dout,
+                                                    float* __restrict__ delta,
+                                                    float* __restrict__ dq_accum, int total,
+                                                    int hq) {
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kRowsPerPass = 256 / kLanesPerRow;
+  constexpr int kTokens = 64;
+  const int h = blockIdx.y;
+  const int sub = threadIdx.x % kLanesPerRow;
+  const int r = threadIdx.x / kLanesPerRow;
+#pragma unroll
+  for (int pass = 0; pass < kTokens / kRowsPerPass; ++pass) {
+    const int t = blockIdx.x * kTokens + pass * kRowsPerPass + r;
+    float acc = 0.0f;
+    if (t < total) {
+      const size_t base = ((size_t)t * hq + h) * D + sub * 8;
+      const auto a = ld16<T>(o + base);
+      const auto b = ld16<T>(dout + base);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += (float)a[i] * (float)b[i];
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(dq_accum + base) = z;
+      *reinterpret_cast<f32x4*>(dq_accum + base + 4) = z;
+    }
+#pragma unroll
+    for (int off = kLanesPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (sub == 0 && t < total) delta[(size_t)h * total + t] = acc;
+  }
+}
+
+// One workgroup per query head: dsink[h] = -sum_t exp(sink[h] - lse[h][t]) * delta[h][t],
+// reduced in a fixed order (per-thread strided sums, then a fixed tree), so
+// the result is deterministic and needs neither atomics nor prior zeroing.
+__global__ __launch_bounds__(256) void dsink_kernel(const float* __restrict__ lse,
+                                                    const float* __restrict__ delta,
+                                                    const float* __restrict__ sink,
+                                                    float* __restrict__ dsink, int total) {
+  __shared__ float part[4];
+  const int h = blockIdx.x;
+  const float s = sink[h];
+  const float* l = lse + (size_t)h * total;
+  const float* dl = delta + (size_t)h * total;
+  float acc = 0.0f;
+  for (int t = threadIdx.x; t < total; t += 256) acc += expf(s - l[t]) * dl[t];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) dsink[h] = -((part[0] + part[1]) + (part[2] + part[3]));
+}
+
+// dq[i] = RNE(dq_accum[i]) for 8 consecutive elements per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ src,
+                                                   T* __restrict__ dst, size_t n8) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(src + 8 * i);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(src + 8 * i + 4);
+  typename V8<T>::type r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    r[k] = to16<T>(a[k]);
+    r[k + 4] = to16<T>(b[k]);
+  }
+  st16<T>(dst + 8 * i, r);
+}
+
+template <typename T, int D>
+static hipError_t preprocess_t(const Problem& p, const void* o, const void* dout,
+                               const float* lse, const float* sink, float* delta,
+                               float* dq_accum, float* dsink, hipStream_t stream) {
+  if (p.total > 0) {
+    dim3 grid((p.total + 63) / 64, p.hq);
+    hipLaunchKernelGGL((delta_kernel<T, D>), grid, dim3(256), 0, stream,
+                       static_cast<const T*>(o), static_cast<const T*>(dout), delta, dq_accum,
+                       p.total, p.hq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (sink == nullptr) return hipSuccess;
+  hipLaunchKernelGGL(dsink_kernel, dim3(p.hq), dim3(256), 0, stream, lse, delta, sink, dsink,
+                     p.total);
+  return hipGetLastError();
+}
+
+hipError_t launch_preprocess(const Problem& p, const void* o, const void* dout, const float* lse,
+                             const float* sink, float* delta, float* dq_accum, float* dsink,
+                             hipStream_t stream) {
+  if (p.bf16)
+    return p.d == 64 ? preprocess_t<__bf16, 64>(p, o, dout, lse, sink, delta, dq_accum, dsink, stream)
+                     : preprocess_t<__bf16, 128>(p, o, dout, lse, sink, delta, dq_accum, dsink, stream);
+  return p.d == 64 ? preprocess_t<_Float16, 64>(p, o, dout, lse, sink, delta, dq_accum, dsink, stream)
+                   : preprocess_t<_Float16, 128>(p, o, dout, lse, sink, delta, dq_accum, dsink, stream);
+}
+
+hipError_t launch_postprocess(const Problem& p, const float* dq_accum, void* dq,
+                              hipStream_t stream) {
+  const size_t n8 = (size_t)p.total * p.hq * p.d / 8;
+  const dim3 grid((unsigned)((n8 + 255) / 256));
+  if (p.bf16)
+    hipLaunchKernelGGL(cast_kernel<__bf16>, grid, dim3(256), 0, stream, dq_accum,
+                       static_cast<__bf16*>(dq), n8);
+  else
+    hipLaunchKernelGGL(cast_kernel<_Float16>, grid, dim3(256), 0, stream, dq_accum,
+                       static_cast<_Float16*>(dq), n8);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,266 @@
+"""Benchmark of the GQA attention backward hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic inputs
+already resident in HBM: attn_fwd -> attn_bwd_preprocess -> attn_bwd ->
+attn_bwd_postprocess, all through the C ABI on the current HIP stream.
+``value`` is the backward throughput of the step: backward FLOPs (the
+convention 2.5 x the forward's 4*B*Hq*N^2*D, halved for causal; sum of L^2
+for varlen; visible pairs for a sliding window) divided by the HIP-event time
+of the three backward launches.  The forward runs in every step (it produces
+O and lse) and is reported separately.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       [--n N] [--seed S] [--no-cpu-baseline] [--no-extra]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import attn_inputs as ai  # noqa: E402
+
+METRIC = "attn_bwd TFLOP/s (fp16/bf16, causal GQA) + MFMA util vs MI355X peak"
+PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+# Pages' number for this exact workload (triton issue "atomic_add slows down
+# attention backwards": fp16, batch 4, 8 heads, d64, causal, N = 32768,
+# atomic_add after vectorized atomics; other hardware -- context only).
+PAGES_BASELINE = {("mha_causal", 32768): 242.346481}
+BWD_SOURCE = os.path.join(ROOT, "atomics_bwd_preprocess_amd", "csrc", "bwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_traffic.json")
+
+
+def bwd_flops(x: dict) -> float:
+    """Backward FLOPs of the main kernel: 10 * Hq * D * (visible pairs)."""
+    lengths = np.asarray(x["lengths"], dtype=np.float64)
+    hq, d, w = x["hq"], x["d"], x["window"]
+    if w > 0:
+        pairs = sum(float(np.minimum(np.arange(L) + 1, w).sum()) for L in x["lengths"])
+    elif x["causal"]:
+        pairs = float((lengths ** 2).sum()) / 2.0
+    else:
+        pairs = float((lengths ** 2).sum())
+    return 10.0 * hq * d * pairs
+
+
+def fwd_flops(x: dict) -> float:
+    return bwd_flops(x) * 4.0 / 10.0
+
+
+def prepost_bytes(x: dict) -> tuple:
+    """Algorithmic HBM bytes of the preprocess and postprocess launches."""
+    rows = float(sum(x["lengths"])) * x["hq"]
+    d, e = x["d"], 2.0
+    pre = rows * d * 2 * e + rows * 4 + rows * d * 4
+    if x["sink"] is not None:
+        pre += rows * 8
+    post = rows * d * (4 + e)
+    return pre, post
+
+
+def _source_hash() -> str:
+    h = hashlib.sha256()
+    for f in (BWD_SOURCE, os.path.join(os.path.dirname(BWD_SOURCE), "common.h")):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload: str):
+    """HBM traffic of the main kernel from committed rocprofv3 counters, if
+    they were taken on the current kernel source; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != _source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def run_gpu(x: dict, steps: int, warmup: int) -> dict:
+    import torch
+
+    from atomics_bwd_preprocess_amd import (attn_bwd, attn_bwd_postprocess, attn_bwd_preprocess,
+                                            path)
+
+    inp = path.to_device(x, "cuda")
+    ws = path.workspace(inp)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for _ in range(warmup):
+        path.step(inp, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        e = ev[i]
+        e[0].record(stream)
+        path.forward(inp, ws)
+        e[1].record(stream)
+        attn_bwd_preprocess(inp.shape, ws.o, inp.do, ws.lse, inp.cu, inp.sink, ws.delta,
+                            ws.dq_accum, ws.dsink)
+        e[2].record(stream)
+        attn_bwd(inp.shape, inp.q, inp.k, inp.v, inp.do, ws.lse, ws.delta, inp.cu, ws.dq_accum,
+                 ws.dk, ws.dv)
+        e[3].record(stream)
+        attn_bwd_postprocess(inp.shape, ws.dq_accum, ws.dq)
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in ev])
+    mean = ms.mean(axis=0)
+    out = dict(wall_ms_per_step=1e3 * wall / steps, fwd_ms=float(mean[0]), pre_ms=float(mean[1]),
+               bwd_ms=float(mean[2]), post_ms=float(mean[3]),
+               bwd_ms_min=float(ms[:, 2].min()), bwd_ms_median=float(np.median(ms[:, 2])))
+    del ws, inp
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(x: dict, min_run_s: float = 4.0) -> dict:
+    """The fp64 oracle (as it stands) on a bounded sample of the workload:
+    one (sequence, query head) of length n_s with its kv head, n_s doubled
+    until one run takes >= min_run_s or reaches the workload's length."""
+    from oracle import attention as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    n_max = max(x["lengths"])
+    n_s = min(1024, n_max)
+    while True:
+        sub = dict(x)
+        sub["q"] = x["q"][:n_s, :1]
+        sub["do"] = x["do"][:n_s, :1]
+        sub["k"] = x["k"][:n_s, :1]
+        sub["v"] = x["v"][:n_s, :1]
+        sub["sink"] = None if x["sink"] is None else x["sink"][:1]
+        sub["cu_seqlens"] = np.array([0, n_s], dtype=np.int32)
+        sub["lengths"] = [n_s]
+        sub["hq"] = sub["hkv"] = 1
+        t0 = time.perf_counter()
+        orc.forward_backward(sub)
+        dt = time.perf_counter() - t0
+        if dt >= min_run_s or n_s >= n_max:
+            break
+        n_s = min(n_max, 2 * n_s)
+    flops = bwd_flops(sub)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"fp64 numpy oracle forward+backward, 1 sequence x 1 head of length {n_s} "
+                       f"(D={x['d']}, causal={x['causal']}, window={x['window']}) taking "
+                       f"{dt:.2f} s; rate = backward FLOPs of that sample / its wall time")}
+
+
+def describe(name: str, x: dict) -> dict:
+    return {"workload": name, "num_seqs": len(x["lengths"]), "max_seqlen": max(x["lengths"]),
+            "total_tokens": int(sum(x["lengths"])), "hq": x["hq"], "hkv": x["hkv"],
+            "head_dim": x["d"], "dtype": x["dtype"], "causal": bool(x["causal"]),
+            "window": x["window"], "sink": x["sink"] is not None}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mha_causal", choices=sorted(ai.WORKLOADS))
+    ap.add_argument("--n", type=int, default=32768, help="sequence length for mha_causal")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the per-workload extras (N sweep and GQA workloads)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+              "path shards by (sequence, kv head) with no collective, so N GPUs would each run "
+              "this benchmark on their own share.", file=sys.stderr)
+        return 2
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+
+    w = ai.workload(args.workload, n=args.n) if args.workload == "mha_causal" else \
+        ai.workload(args.workload)
+    x = ai.generate(w, args.seed)
+    r = run_gpu(x, args.steps, args.warmup)
+    fl = bwd_flops(x)
+    bwd_total_ms = r["pre_ms"] + r["bwd_ms"] + r["post_ms"]
+    value = fl / (bwd_total_ms * 1e-3) / 1e12
+    kernel_tflops = fl / (r["bwd_ms"] * 1e-3) / 1e12
+    traffic = _traffic(w.name if w.name != "mha_causal" else f"mha_causal_n{args.n}")
+    pre_b, post_b = prepost_bytes(x)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["fwd_ms"] + bwd_total_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": x["dtype"],
+        "data": "synthetic (seeded N(0, sigma^2) inputs of the workload's shape)",
+        "config": describe(w.name, x),
+        "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 3),
+                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(kernel_tflops / PEAK_MFMA_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "attn_bwd main kernel", "flops_per_launch": fl,
+                     "avg_launch_ms": round(r["bwd_ms"], 4)},
+        "kernels_ms": {"attn_fwd": round(r["fwd_ms"], 4),
+                       "attn_bwd_preprocess": round(r["pre_ms"], 4),
+                       "attn_bwd": round(r["bwd_ms"], 4),
+                       "attn_bwd_postprocess": round(r["post_ms"], 4)},
+        "hbm_gbs": {"attn_bwd_preprocess": round(pre_b / (r["pre_ms"] * 1e-3) / 1e9, 1),
+                    "attn_bwd_postprocess": round(post_b / (r["post_ms"] * 1e-3) / 1e9, 1),
+                    "peak": PEAK_HBM_GBS},
+        "fwd_tflops": round(fwd_flops(x) / (r["fwd_ms"] * 1e-3) / 1e12, 3),
+        "wall_ms_per_step": round(r["wall_ms_per_step"], 4),
+    }
+    base = PAGES_BASELINE.get((w.name, args.n if w.name == "mha_causal" else None))
+    if base:
+        line["vs_baseline"] = round(value / base, 4)
+        line["baseline_note"] = ("pages' number for this workload on other hardware (triton issue "
+                                 "4717, atomic_add after vectorized atomics): context only")
+    if not args.no_extra:
+        extra = {}
+        cases = [("mha_causal", n) for n in ai.MHA_SWEEP if n != args.n or w.name != "mha_causal"]
+        cases += [(nm, None) for nm in ("varlen_gqa", "sink_window", "long_gqa")
+                  if nm != w.name]
+        for nm, n in cases:
+            wx = ai.workload(nm, n=n) if n else ai.workload(nm)
+            xx = ai.generate(wx, args.seed)
+            rr = run_gpu(xx, max(3, args.steps // 4), 2)
+            f = bwd_flops(xx)
+            key = f"{nm}_n{n}" if n else nm
+            extra[key] = {"bwd_tflops": round(f / ((rr["pre_ms"] + rr["bwd_ms"] + rr["post_ms"])
+                                                   * 1e-3) / 1e12, 2),
+                          "attn_bwd_kernel_tflops": round(f / (rr["bwd_ms"] * 1e-3) / 1e12, 2),
+                          "attn_bwd_ms": round(rr["bwd_ms"], 4),
+                          "frac": round(f / (rr["bwd_ms"] * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
+            print(f"bench: {key}: {extra[key]}", file=sys.stderr, flush=True)
+        line["per_workload"] = extra
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

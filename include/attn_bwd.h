@@ -1,0 +1,150 @@
+/*
+ * attn_bwd.h -- C ABI of the MI355X (gfx950) GQA attention backward library.
+ *
+ * The library computes the FlashAttention-style backward pass of grouped-query
+ * attention over packed variable-length sequences, with causal and
+ * sliding-window masks and a per-head attention sink, plus the forward pass
+ * that produces the O and lse the backward consumes.  Sources for the
+ * operations are given per call below; "the pages" are
+ *   [TL]  tilelang PR "[GQA] Add regional atomic add to slightly boost performance",
+ *   [ASC] tilelang-ascend PR "GQA Sink Backward BHSD",
+ *   [TRI] triton issue "atomic_add slows down attention backwards due to layout conversions".
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are packed "THD": all tokens of all sequences along one axis,
+ *    heads next, head_dim innermost and contiguous.
+ *      q, o, dout, dq      [T, Hq,  D]   storage dtype (fp16 or bf16)
+ *      k, v, dk, dv        [T, Hkv, D]   storage dtype
+ *      lse, delta          [Hq, T]       fp32 (lse: natural log)
+ *      dq_accum            [T, Hq, D]    fp32 workspace for dQ accumulation
+ *      sink, dsink         [Hq]          fp32
+ *      cu_seqlens          [num_seqs+1]  int32, sequence s spans tokens
+ *                                        [cu_seqlens[s], cu_seqlens[s+1])
+ *  - All pointers are DEVICE pointers owned by the caller.  The library never
+ *    allocates, frees or retains them and keeps no state between calls.
+ *  - Every call only enqueues work on `stream` (NULL = the default stream) and
+ *    never synchronises; buffers must stay alive until that work completes.
+ *  - Query head h reads kv head h / (Hq/Hkv) (contiguous groups, [TL] review
+ *    comment on the single dK/dV write).
+ *  - Masks (per sequence, query position i, key position j, both local):
+ *      causal:      j <= i
+ *      window W>0:  i - W < j <= i  (requires causal; at most W keys per query)
+ *  - Sink ([ASC] forward with online softmax + sink + window): one logit per
+ *    query head in the units of scaled scores; it joins the softmax
+ *    denominator and has no value vector, so
+ *      lse_i = log(sum_{visible j} exp(scale*q_i.k_j) + exp(sink_h)).
+ *  - Alignment: q, k, v, o, dout, dq, dk, dv and dq_accum must be 16-byte
+ *    aligned; lse, delta, sink, dsink and cu_seqlens 4-byte aligned.
+ *  - Errors: argument problems are reported by the return code before any
+ *    work is enqueued (nothing is launched on error); a launch failure returns
+ *    ATTN_ERR_HIP.  attn_last_error() gives a message for the calling thread.
+ *    Device-side faults surface at the caller's next synchronisation.
+ *  - Device-data preconditions (documented, not checked because the data is
+ *    device-resident): cu_seqlens[0] = 0, non-decreasing, last entry =
+ *    total_tokens, every length <= max_seqlen.  Kernels clamp sequence bounds
+ *    to [0, total_tokens], so a violation gives wrong results, never an
+ *    out-of-bounds access.  A NULL cu_seqlens means a dense batch:
+ *    sequence s spans [s*max_seqlen, (s+1)*max_seqlen) and
+ *    total_tokens must equal num_seqs*max_seqlen.
+ */
+#ifndef ATTN_BWD_H
+#define ATTN_BWD_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null pointer, misalignment, bad dims, Hq % Hkv != 0,
+                               window without causal, sink/dsink mismatch */
+  ATTN_ERR_UNSUPPORTED = 2, /* head_dim not in {64, 128}, unknown dtype */
+  ATTN_ERR_HIP = 3          /* a HIP launch reported an error */
+} attn_status_t;
+
+typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+/* Problem description shared by every call. */
+typedef struct {
+  int32_t num_seqs;     /* number of packed sequences (>= 1) */
+  int32_t max_seqlen;   /* upper bound on every sequence length (>= 1) */
+  int32_t total_tokens; /* T: rows of q/k/v (>= 0) */
+  int32_t hq;           /* query heads */
+  int32_t hkv;          /* key/value heads; hq % hkv == 0 */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int32_t causal;       /* 0 or 1 */
+  int32_t window;       /* 0: none; W > 0: sliding window (requires causal) */
+  float scale;          /* score scale, typically 1/sqrt(D); finite and > 0 */
+  int32_t dtype;        /* attn_dtype_t of q/k/v/o/dout/dq/dk/dv */
+} attn_shape_t;
+
+/*
+ * Forward ([ASC] forward kernel: online softmax with sink and window).
+ * Writes O [T,Hq,D] (storage dtype, RNE from fp32) and lse [Hq,T] (fp32,
+ * natural log).  sink may be NULL (no sink).  A row with no visible key and
+ * no sink gets O = 0 and lse = -inf (cannot happen with causal masks, where a
+ * query always sees itself).
+ */
+attn_status_t attn_fwd(const attn_shape_t* shape, const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens, const float* sink, void* o, float* lse,
+                       hipStream_t stream);
+
+/*
+ * Backward preprocess ([ASC] merged "flashattn_bwd_preprocess" with the dsink
+ * kernel; Phase 0 of its single backward kernel computes Delta as the row sum
+ * of O*dO; the Dsink kernel computes dsink = -sum exp(sink - lse) * Delta).
+ *   delta[h][t]  = sum_d o[t][h][d] * dout[t][h][d]   (fp32 accumulation)
+ *   dq_accum     := 0 (all T*Hq*D entries)
+ *   dsink[h]     = -sum_t exp(sink[h] - lse[h][t]) * delta[h][t]
+ * sink and dsink must both be NULL or both non-NULL.  dsink is written (not
+ * accumulated) and its reduction order is fixed, so it is deterministic.
+ */
+attn_status_t attn_bwd_preprocess(const attn_shape_t* shape, const void* o, const void* dout,
+                                  const float* lse, const int32_t* cu_seqlens,
+                                  const float* sink, float* delta, float* dq_accum,
+                                  float* dsink, hipStream_t stream);
+
+/*
+ * Backward main pass.  Recomputes S = Q K^T and P = exp(S*scale - lse) per
+ * tile, then dV = P^T dO, dP = dO V^T, dS = P o (dP - Delta) * scale,
+ * dK = dS^T Q and dQ = dS K ([ASC] review thread, kernels k1-k5 fused;
+ * spec formulas).
+ *  - dq_accum (zeroed by attn_bwd_preprocess) receives dQ through fp32
+ *    atomic adds issued once per (query tile, key tile) as one coalesced
+ *    region-wide sweep ([TL] regional atomic add; [TRI] atomics issued from
+ *    the matrix-core layout).  Summation order varies run to run.
+ *  - dk, dv are WRITTEN once per key row after accumulating, in fp32
+ *    registers, over every query block and every query head of the group
+ *    ([TL] review: accumulate locally, write once).  They are deterministic.
+ * The sink enters only through lse.
+ */
+attn_status_t attn_bwd(const attn_shape_t* shape, const void* q, const void* k, const void* v,
+                       const void* dout, const float* lse, const float* delta,
+                       const int32_t* cu_seqlens, float* dq_accum, void* dk, void* dv,
+                       hipStream_t stream);
+
+/*
+ * Backward postprocess ([ASC] postprocess kernel casting the fp32 gradient
+ * accumulator): dq[t][h][d] = RNE cast of dq_accum[t][h][d] to the storage dtype.
+ */
+attn_status_t attn_bwd_postprocess(const attn_shape_t* shape, const float* dq_accum, void* dq,
+                                   hipStream_t stream);
+
+/* Static text for a status code. */
+const char* attn_status_string(attn_status_t status);
+/* Detail of the calling thread's most recent error ("" if none). */
+const char* attn_last_error(void);
+/* ATTN_ABI_VERSION of the built library. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_BWD_H */

@@ -1,0 +1,113 @@
+"""The C-ABI library: it loads, exports every entry point the header declares,
+and rejects bad arguments with status codes before launching anything (so
+these run without a GPU: no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import atomics_bwd_preprocess_amd as ab
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_bwd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ab.LIB_PATH),
+                                reason="libattn_bwd.so not built (run __graft_entry__.build())")
+
+FAKE = 0x10000  # a 16-byte-aligned, never dereferenced address
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:attn_status_t|const char\*|int)\s+(attn_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(["attn_fwd", "attn_bwd_preprocess", "attn_bwd",
+                                  "attn_bwd_postprocess", "attn_status_string",
+                                  "attn_last_error", "attn_abi_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    L = ab.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert ab.attn_abi_version() == 1
+    assert L.attn_status_string(0) == b"ok"
+    assert L.attn_status_string(1) == b"invalid argument"
+
+
+def _shape(**kw):
+    base = dict(num_seqs=2, max_seqlen=64, total_tokens=128, hq=4, hkv=2, head_dim=64, causal=1,
+                window=0, scale=0.125, dtype=0)
+    base.update(kw)
+    return ab.Shape(**{k: v for k, v in base.items()})
+
+
+def _fwd(shape, q=FAKE, k=FAKE, v=FAKE, cu=None, sink=None, o=FAKE, lse=FAKE):
+    return ab.lib().attn_fwd(ctypes.byref(shape), q, k, v, cu, sink, o, lse, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=3, hkv=2), 1),
+    (dict(hkv=0), 1),
+    (dict(num_seqs=0), 1),
+    (dict(max_seqlen=0), 1),
+    (dict(total_tokens=-1), 1),
+    (dict(head_dim=96), 2),
+    (dict(head_dim=256), 2),
+    (dict(dtype=7), 2),
+    (dict(causal=0, window=16), 1),
+    (dict(window=-1), 1),
+    (dict(causal=2), 1),
+    (dict(scale=0.0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(total_tokens=100), 1),  # dense batch without cu_seqlens needs T = B * N
+])
+def test_shape_validation(kw, status):
+    assert _fwd(_shape(**kw)) == status
+    assert ab.lib().attn_last_error().decode() != ""
+
+
+def test_pointer_validation():
+    s = _shape()
+    assert _fwd(s, q=None) == 1
+    assert b"q is NULL" in ab.lib().attn_last_error()
+    assert _fwd(s, k=FAKE + 8) == 1
+    assert b"aligned" in ab.lib().attn_last_error()
+    assert _fwd(s, lse=None) == 1
+    L = ab.lib()
+    # preprocess: sink without dsink
+    assert L.attn_bwd_preprocess(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None,
+                                 None) == 1
+    assert b"sink and dsink" in L.attn_last_error()
+    # backward: missing dv
+    assert L.attn_bwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
+                      None) == 1
+    # postprocess: misaligned dq
+    assert L.attn_bwd_postprocess(ctypes.byref(s), FAKE, FAKE + 2, None) == 1
+    assert L.attn_bwd_postprocess(None, FAKE, FAKE, None) == 1
+
+
+def test_empty_problem_launches_nothing():
+    # total_tokens = 0 with explicit cu_seqlens: valid, returns OK without a launch.
+    s = _shape(total_tokens=0)
+    assert _fwd(s, cu=FAKE) == 0
+    L = ab.lib()
+    assert L.attn_bwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                      None) == 0
+    assert L.attn_bwd_postprocess(ctypes.byref(s), FAKE, FAKE, None) == 0
+    assert L.attn_bwd_preprocess(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
+                                 None) == 0
+    assert L.attn_last_error() == b""
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+
+    s = _shape()
+    q = torch.zeros(128, 4, 64, dtype=torch.float16)
+    with pytest.raises(ab.AttnError):
+        ab.attn_bwd_postprocess(s, torch.zeros(128, 4, 64), q)
