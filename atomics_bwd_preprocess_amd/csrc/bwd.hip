@@ -1,34 +1,47 @@
 // Attention backward main pass for grouped-query attention (key/value
 // stationary), gfx950.
 //
-// Per (query tile i, key tile j) the pass recomputes S = Q K^T and
+// Per (query tile, key tile) the pass recomputes S = Q K^T and
 // P = exp(S * scale - lse), then forms dV += P^T dO, dP = dO V^T,
 // dS = P o (dP - Delta) * scale, dK += dS^T Q and the dQ partial dS K
 // (tilelang-ascend PR "GQA Sink Backward BHSD": review thread listing kernels
 // k1-k5, fused here into one loop body as in its single-kernel revision).
 //
-// Work decomposition: one workgroup (4 waves) owns one (sequence, kv head g,
-// key block of 128 rows); wave w owns keys [32w, 32w + 32) of the block.
-//  * K and V rows of the wave live in registers as MFMA B operands for the
-//    S and dP products; K is also staged transposed in LDS for dQ.
-//  * The loop runs over every query head of the group and, per head, over
-//    every query block (64 rows) that can see the key block under the causal
-//    / window masks.  dK and dV accumulate in fp32 registers across the whole
-//    loop and are written once at the end, with no atomics (tilelang PR
-//    "[GQA] Add regional atomic add": review comment on accumulating dK/dV
-//    fragments across the loop and writing once).
-//  * S and dP are computed with the key index in the lane (MFMA column), so P
-//    and dS feed the dV / dK products straight from registers.  dS is stored
-//    once to LDS (query-major) for dQ = dS K, whose 64 x D result is split
-//    over the 4 waves.
-//  * dQ partials leave through fp32 atomic adds issued directly from the
-//    MFMA C layout: one register = two query rows x 32 consecutive
-//    dimensions, i.e. two fully used 128-byte segments per wave instruction
+// Work decomposition.  One workgroup (8 waves, two per SIMD) owns one
+// (sequence, kv head g, block of 256 keys); wave w owns keys [32w, 32w + 32)
+// as one 32-key MFMA tile.  The loop runs over every query head of the
+// group and, per head, over every query block that can see the key block
+// under the causal / window masks ("pairs").
+//  * dK and dV of the wave's 32 keys accumulate in fp32 registers over the
+//    whole loop -- every query block of every head of the group -- and are
+//    written once at the end, with no atomics (tilelang PR "[GQA] Add
+//    regional atomic add": review comment on accumulating dK/dV fragments
+//    across the loop and writing once).
+//  * dQ partials leave through fp32 atomic adds issued straight from the
+//    MFMA C layout, one sweep per pair: each wave owns two 16 x 16 tiles of
+//    the pair's dQ block, and one register of a tile = four query rows x 16
+//    consecutive dims, four fully used 64-byte segments per wave instruction
 //    (tilelang PR: one region-wide atomic per tile instead of per-element
-//    loops; triton issue "atomic_add slows down attention backwards": avoid a
-//    layout conversion before the atomics and vectorise them).
+//    loops; triton issue "atomic_add slows down attention backwards": no
+//    layout conversion before the atomics, vectorised updates).
+//    Device-scope fp32 atomics resolve at the memory side on this part, so
+//    their bytes per FLOP (4 * BM * D per 10 * BM * BN * D) set a ceiling;
+//    256 keys per workgroup halve them relative to 128.
+//
+// Data movement.  K is staged once into LDS (needed as the dQ operand); V
+// (and K for D = 64) of the wave live in registers as MFMA B operands.
+// Q / dO tiles of a pair (row-major, XOR-swizzled 16-byte chunks) and their
+// lse / Delta rows are double-buffered in LDS and prefetched through
+// registers: the loads for pair i + 2 are issued before the atomics of pair
+// i, so they never queue behind them.  Transposed operands (dO, Q for
+// dV / dK; dS, K for dQ) come from gfx950's transposing LDS read, and dS is
+// stored key-major with 8-byte writes.  All LDS patterns are bank-conflict
+// free (the swizzles are modelled by the host tests of the LDS layout).
+// One workgroup barrier per pair.
 //
 // The sink needs no term here: it only enters through lse.
+#include <limits.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -36,8 +49,34 @@ namespace attn {
 
 namespace {
 
-constexpr int kBM = 64;   // query rows per step
-constexpr int kBN = 128;  // key rows per workgroup (4 waves x 32)
+constexpr int kNW = 8;               // waves per workgroup (2 per SIMD)
+constexpr int kKT = 1;               // 32-key MFMA tiles per wave
+constexpr int kThreads = 64 * kNW;
+constexpr int kBN = kNW * 32 * kKT;  // keys per workgroup
+
+template <int D>
+struct Cfg {
+  static constexpr int BM = D == 128 ? 32 : 64;  // query rows per pair
+  static constexpr int MT = BM / 32;             // 32-row query tiles
+  static constexpr int NT = D / 32;              // 32-wide dim tiles
+  static constexpr bool KREG = D == 64;          // K of the wave also in registers
+  // LDS map (bytes)
+  static constexpr int K_OFF = 0;
+  static constexpr int QT = BM * D * 2;
+  static constexpr int Q_OFF = K_OFF + kBN * D * 2;
+  static constexpr int DO_OFF = Q_OFF + 2 * QT;
+  static constexpr int DST = kBN * BM * 2;
+  static constexpr int DS_OFF = DO_OFF + 2 * QT;
+  static constexpr int LSE_OFF = DS_OFF + 2 * DST;
+  static constexpr int DLT_OFF = LSE_OFF + 2 * BM * 4;
+  static constexpr int BYTES = DLT_OFF + 2 * BM * 4;
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int PF = BM * CH / kThreads;      // prefetch chunks per thread per tensor
+  static constexpr int NQT = BM / 16, NDT = D / 16;  // 16x16 dQ tiles
+  static_assert(NQT * NDT == 2 * kNW, "two 16x16 dQ tiles per wave");
+  static_assert(PF >= 1 && BM * CH % kThreads == 0, "prefetch split");
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
 
 struct BwdArgs {
   const void* q;
@@ -55,60 +94,63 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
-template <typename T, int D>
-struct BwdSmem {
-  alignas(16) T q[kBM][D + 8];     // Q_i, query-major
-  alignas(16) T dout[kBM][D + 8];  // dO_i, query-major
-  alignas(16) T qt[D][kBM + 8];    // Q_i transposed
-  alignas(16) T dot[D][kBM + 8];   // dO_i transposed
-  alignas(16) T ds[kBM][kBN + 8];  // dS, query-major
-  alignas(16) T kt[D][kBN + 8];    // K_j transposed
-  float lse2[kBM];                 // lse * log2(e); +inf outside the sequence
-  float delta[kBM];
-};
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Stage a [kBM x D] tile (rows r0.., zero-filled past `L`) into a row-major
-// and a transposed LDS copy.  A unit is 4 rows x 8 dims: four 16-byte global
-// loads, four 16-byte row-major stores and eight 8-byte transposed stores.
-template <typename T, int D>
-__device__ __forceinline__ void stage_tile(const T* __restrict__ src, size_t row_stride,
-                                           int r0, int L, T (*rm)[D + 8], T (*tr)[kBM + 8],
-                                           int tid) {
-  using T8 = typename V8<T>::type;
-  using T4 = typename V8<T>::half_type;
-  for (int u = tid; u < (kBM / 4) * (D / 8); u += 256) {
-    const int rg = u / (D / 8), dc = u % (D / 8);
-    T8 rows[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = r0 + 4 * rg + e;
-      rows[e] = r < L ? ld16<T>(src + (size_t)r * row_stride + 8 * dc) : zero8<T>();
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) st16<T>(&rm[4 * rg + e][8 * dc], rows[e]);
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      T4 col;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) col[e] = rows[e][dd];
-      st8<T>(&tr[8 * dc + dd][4 * rg], col);
-    }
-  }
+// Row-major tiles: 16-byte chunk c of row r lives at chunk
+// (c & ~7) | ((c & 7) ^ chunk_swz(r)).
+__device__ __forceinline__ int chunk_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+template <int D>
+__device__ __forceinline__ int rm_off(int r, int col) {  // col: multiple of 4
+  const int c = col >> 3;
+  return r * (D * 2) + (((c & ~7) | ((c & 7) ^ chunk_swz(r))) << 4) + ((col & 7) << 1);
+}
+// Key-major dS tile: 8-byte slot s of row r lives at slot s ^ slot_swz(r).
+template <int BM>
+__device__ __forceinline__ int slot_swz(int r) {
+  return BM == 32 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
+}
+template <int BM>
+__device__ __forceinline__ int dst_off(int r, int q) {  // q: multiple of 4
+  return r * (BM * 2) + (((q >> 2) ^ slot_swz<BM>(r)) << 3);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// i receives element (i % 4) of the 8-byte pieces addressed by lanes
+// 4e + i / 4, e = 0..3.  Lanes address row k0 + p / 4, columns n0 + 4 (p % 4)
+// (p = lane % 16) of a row-major matrix; lane i then holds rows k0..k0+3 of
+// column n0 + i.
+__device__ __forceinline__ u32x2 tr_read(const char* smem, int off) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + off));
+  return __builtin_bit_cast(u32x2, v);
+}
+template <typename T>
+__device__ __forceinline__ typename V8<T>::type tr_pair(const char* smem, int off_lo, int off_hi) {
+  const u32x2 lo = tr_read(smem, off_lo), hi = tr_read(smem, off_hi);
+  const u32x4 r = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(typename V8<T>::type, r);
+}
+
+template <typename T>
+__device__ __forceinline__ typename V8<T>::type lds16(const char* smem, int off) {
+  return __builtin_bit_cast(typename V8<T>::type, *reinterpret_cast<const u32x4*>(smem + off));
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs p) {
+__global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
+  using C = Cfg<D>;
   using T8 = typename V8<T>::type;
   using T4 = typename V8<T>::half_type;
-  __shared__ BwdSmem<T, D> sm;
+  constexpr int BM = C::BM, MT = C::MT, NT = C::NT;
+  __shared__ __attribute__((aligned(16))) char smem[C::BYTES];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, n = lane & 31, c = lane >> 5;
+  const int l16 = lane & 15, g16 = (lane >> 4) & 1;
 
-  // Block order: key-block index slowest, so every (sequence, kv head) gets
-  // its largest causal workload (key block 0) first, and the blocks of one
-  // (sequence, kv head) are a multiple of 8 apart whenever num_seqs * Hkv is,
-  // which keeps them on one XCD and its L2.
+  // Key-block index slowest: every (sequence, kv head) starts with its
+  // largest causal workload, and the blocks of one (sequence, kv head) stay
+  // a multiple of 8 apart whenever num_seqs * Hkv is (same XCD and L2).
   const int nsg = p.num_seqs * p.hkv;
   const int jb = blockIdx.x / nsg;
   const int rem = blockIdx.x % nsg;
@@ -119,184 +161,268 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs p) {
   const int kv0 = jb * kBN;
   if (kv0 >= L) return;
   const int G = p.hq / p.hkv;
+  const uint32_t kv_row = (uint32_t)p.hkv * D;  // elements between key rows
+  const uint32_t q_row = (uint32_t)p.hq * D;    // elements between query rows
+  const int nkeys = min(L - kv0, kBN);          // valid keys of this block
 
-  const T* __restrict__ qp = static_cast<const T*>(p.q);
-  const T* __restrict__ kp = static_cast<const T*>(p.k);
-  const T* __restrict__ vp = static_cast<const T*>(p.v);
-  const T* __restrict__ dop = static_cast<const T*>(p.dout);
-  const size_t kv_stride = (size_t)p.hkv * D;
-  const size_t q_stride = (size_t)p.hq * D;
+  // Buffer resources over this block's keys: rows past the sequence end read
+  // as zero and their stores are dropped.
+  const size_t kv_base = ((size_t)(a + kv0) * p.hkv + g) * D;
+  const rsrc_t kr = make_rsrc(static_cast<const T*>(p.k) + kv_base, nkeys * kv_row * 2);
+  const rsrc_t vr = make_rsrc(static_cast<const T*>(p.v) + kv_base, nkeys * kv_row * 2);
 
-  // Keys of this lane: B-operand column n of wave w.
-  const int kj = kv0 + 32 * w + n;
-  T8 kreg[D / 16], vreg[D / 16];
-  {
-    const size_t off = (size_t)(a + kj) * kv_stride + (size_t)g * D + 8 * c;
+  // ---- K block into LDS ------------------------------------------------------
+#pragma unroll 4
+  for (int u = tid; u < kBN * C::CH; u += kThreads) {
+    const int r = u / C::CH, ch = u % C::CH;
+    *reinterpret_cast<u32x4*>(smem + C::K_OFF + rm_off<D>(r, 8 * ch)) =
+        buf_load16(kr, (r * kv_row + 8 * ch) * 2);
+  }
+  // ---- V (and K for D = 64) of this wave's keys as MFMA B operands ---------
+  T8 vreg[kKT][D / 16];
+  T8 kreg[C::KREG ? kKT : 1][C::KREG ? D / 16 : 1];
+#pragma unroll
+  for (int kt = 0; kt < kKT; ++kt) {
+    const uint32_t row = 32 * kKT * w + 32 * kt + n;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      kreg[ks] = kj < L ? ld16<T>(kp + off + 16 * ks) : zero8<T>();
-      vreg[ks] = kj < L ? ld16<T>(vp + off + 16 * ks) : zero8<T>();
-    }
-  }
-  // K_j transposed into LDS (a unit is 4 keys x 8 dims).
-  for (int u = tid; u < (kBN / 4) * (D / 8); u += 256) {
-    const int rg = u / (D / 8), dc = u % (D / 8);
-    T8 rows[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = kv0 + 4 * rg + e;
-      rows[e] = j < L ? ld16<T>(kp + (size_t)(a + j) * kv_stride + (size_t)g * D + 8 * dc)
-                      : zero8<T>();
-    }
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      T4 col;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) col[e] = rows[e][dd];
-      st8<T>(&sm.kt[8 * dc + dd][4 * rg], col);
+      const uint32_t off = (row * kv_row + 16 * ks + 8 * c) * 2;
+      vreg[kt][ks] = __builtin_bit_cast(T8, buf_load16(vr, off));
+      if constexpr (C::KREG) kreg[kt][ks] = __builtin_bit_cast(T8, buf_load16(kr, off));
     }
   }
 
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x16 dk[kKT][NT], dv[kKT][NT];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
-    dk[t] = f32x16{};
-    dv[t] = f32x16{};
-  }
+  for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      dk[kt][t] = f32x16{};
+      dv[kt][t] = f32x16{};
+    }
 
-  // Query blocks that can see any key of this block.
-  const int kv_last = min(L, kv0 + kBN) - 1;
-  const int ib0 = p.causal ? kv0 / kBM : 0;
-  int ib1 = (L + kBM - 1) / kBM;
-  if (p.window > 0) ib1 = min(ib1, (kv_last + p.window - 1) / kBM + 1);
-  const int wk_lo = kv0 + 32 * w, wk_hi = wk_lo + 31;
+  // ---- pairs: (query head of the group) x (query blocks that see the keys)
+  const int kv_last = kv0 + nkeys - 1;
+  const int ib0 = p.causal ? kv0 / BM : 0;
+  int ib1 = (L + BM - 1) / BM;
+  if (p.window > 0) ib1 = min(ib1, (kv_last + p.window - 1) / BM + 1);
+  const int nq = ib1 - ib0;
+  const int npairs = G * nq;
+  const int wk_lo = kv0 + 32 * kKT * w;
 
-  // dQ tiles of this wave: D = 128 -> column tile w, both row tiles;
-  // D = 64 -> row tile w / 2, column tile w % 2.
-  constexpr int kDqTiles = D / 64;
-  const int dq_nt = D == 128 ? w : (w & 1);
-  const int dq_mt0 = D == 128 ? 0 : (w >> 1);
+  // Prefetch registers: PF chunks of Q and of dO per thread, plus lse / Delta.
+  u32x4 pq[C::PF], pdo[C::PF];
+  float plse = 0.0f, pdlt = 0.0f;
+  auto load_pair = [&](int i) {
+    const int h = g * G + i / nq;
+    const int q0 = (ib0 + i % nq) * BM;
+    const int rows = max(0, min(L - q0, BM));
+    const size_t qb = ((size_t)(a + q0) * p.hq + h) * D;
+    const rsrc_t qr = make_rsrc(static_cast<const T*>(p.q) + qb, rows * q_row * 2);
+    const rsrc_t dr = make_rsrc(static_cast<const T*>(p.dout) + qb, rows * q_row * 2);
+#pragma unroll
+    for (int u = 0; u < C::PF; ++u) {
+      const int ci = tid + kThreads * u;
+      const uint32_t off = ((ci / C::CH) * q_row + 8 * (ci % C::CH)) * 2;
+      pq[u] = buf_load16(qr, off);
+      pdo[u] = buf_load16(dr, off);
+    }
+    if (tid < BM) {
+      const size_t idx = (size_t)h * p.total + a + q0;
+      const float l = buf_load_f32(make_rsrc(p.lse + idx, rows * 4), tid * 4);
+      pdlt = buf_load_f32(make_rsrc(p.delta + idx, rows * 4), tid * 4);
+      // rows outside the sequence (or that saw nothing) get P = 0
+      plse = (tid >= rows || l == -INFINITY) ? INFINITY : l * kLog2e;
+    }
+  };
+  auto store_pair = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < C::PF; ++u) {
+      const int ci = tid + kThreads * u;
+      const int o = rm_off<D>(ci / C::CH, 8 * (ci % C::CH));
+      *reinterpret_cast<u32x4*>(smem + C::Q_OFF + buf * C::QT + o) = pq[u];
+      *reinterpret_cast<u32x4*>(smem + C::DO_OFF + buf * C::QT + o) = pdo[u];
+    }
+    if (tid < BM) {
+      reinterpret_cast<float*>(smem + C::LSE_OFF)[buf * BM + tid] = plse;
+      reinterpret_cast<float*>(smem + C::DLT_OFF)[buf * BM + tid] = pdlt;
+    }
+  };
 
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = g * G + hh;
-    const T* qh = qp + (size_t)a * q_stride + (size_t)h * D;
-    const T* doh = dop + (size_t)a * q_stride + (size_t)h * D;
-    for (int ib = ib0; ib < ib1; ++ib) {
-      const int q0 = ib * kBM;
-      __syncthreads();  // the previous step is done with every LDS tile
-      stage_tile<T, D>(qh, q_stride, q0, L, sm.q, sm.qt, tid);
-      stage_tile<T, D>(doh, q_stride, q0, L, sm.dout, sm.dot, tid);
-      if (tid < kBM) {
-        const int r = q0 + tid;
-        const size_t idx = (size_t)h * p.total + a + r;
-        const float l = r < L ? p.lse[idx] : -INFINITY;
-        // Rows outside the sequence, and rows that saw nothing (lse = -inf),
-        // get P = 0 through lse2 = +inf.
-        sm.lse2[tid] = l == -INFINITY ? INFINITY : l * kLog2e;
-        sm.delta[tid] = r < L ? p.delta[idx] : 0.0f;
+  load_pair(0);
+  store_pair(0);
+  if (npairs > 1) load_pair(1);
+  __syncthreads();
+
+  // dQ tiles of this wave (16x16x32 MFMA): query tile dq_qt, dim tiles dq_dt
+  // and dq_dt + 1.  C layout: lane l holds dim l % 16 of rows 4 (l / 16) + r.
+  const int dq_qt = (2 * w) / C::NDT, dq_dt = (2 * w) % C::NDT;
+  const int g64 = lane >> 4;  // 16-lane group = k-slot group of the 16x16x32 operands
+  const uint32_t dq_lane_off = ((16 * dq_qt + 4 * g64) * q_row + 16 * dq_dt + l16) * 4;
+
+  for (int i = 0; i < npairs; ++i) {
+    const int buf = i & 1;
+    const int h = g * G + i / nq;
+    const int q0 = (ib0 + i % nq) * BM;
+    const char* qs = smem + C::Q_OFF + buf * C::QT;
+    const char* dos = smem + C::DO_OFF + buf * C::QT;
+    char* dss = smem + C::DS_OFF + buf * C::DST;
+    const float* lse2 = reinterpret_cast<const float*>(smem + C::LSE_OFF) + buf * BM;
+    const float* dlt = reinterpret_cast<const float*>(smem + C::DLT_OFF) + buf * BM;
+
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) {
+      // Keys [tk_lo, tk_lo + 32) of this wave's tile kt against queries [q0, q0 + BM).
+      const int tk_lo = wk_lo + 32 * kt, tk_hi = tk_lo + 31;
+      const bool empty = tk_lo >= L || q0 >= L || (p.causal && tk_lo > q0 + BM - 1) ||
+                         (p.window > 0 && tk_hi <= q0 - p.window);
+      if (empty) {
+        const u32x2 z = {0u, 0u};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<u32x2*>(dss + dst_off<BM>(32 * kKT * w + 32 * kt + n, 32 * mt + 8 * g4 + 4 * c)) = z;
+        continue;
       }
-      __syncthreads();
-
-      // S = Q K^T and dP = dO V^T for 64 queries x this wave's 32 keys.
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
-      f32x16 pacc[2] = {f32x16{}, f32x16{}};
+      // -- S = Q K^T and dP = dO V^T: [BM queries] x [32 keys]
+      f32x16 sacc[MT], pacc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        sacc[mt] = f32x16{};
+        pacc[mt] = f32x16{};
+      }
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
+        T8 kb;
+        if constexpr (C::KREG)
+          kb = kreg[kt][ks];
+        else
+          kb = lds16<T>(smem, C::K_OFF + rm_off<D>(32 * kKT * w + 32 * kt + n, 16 * ks + 8 * c));
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          sacc[mt] = mfma32(ld16<T>(&sm.q[32 * mt + n][16 * ks + 8 * c]), kreg[ks], sacc[mt]);
-          pacc[mt] = mfma32(ld16<T>(&sm.dout[32 * mt + n][16 * ks + 8 * c]), vreg[ks], pacc[mt]);
+        for (int mt = 0; mt < MT; ++mt) {
+          const int o = rm_off<D>(32 * mt + n, 16 * ks + 8 * c);
+          sacc[mt] = mfma32(lds16<T>(qs, o), kb, sacc[mt]);
+          pacc[mt] = mfma32(lds16<T>(dos, o), vreg[kt][ks], pacc[mt]);
         }
       }
 
-      // P = exp2(S * scale * log2e - lse * log2e); dS = P (dP - Delta) scale.
-      const bool full = (q0 + kBM <= L) && (wk_hi < L) && (!p.causal || wk_hi <= q0) &&
-                        (p.window <= 0 || wk_lo > q0 + kBM - 1 - p.window);
+      // -- P = exp2(S scale log2e - lse log2e); dS = P (dP - Delta) scale
+      const bool full = (q0 + BM <= L) && (tk_hi < L) && (!p.causal || tk_hi <= q0) &&
+                        (p.window <= 0 || tk_lo > q0 + BM - 1 - p.window);
+      // Visible iff lo <= q - k <= hi and k < L (branch-free per element).
+      const int kj = tk_lo + n;
+      const int dlo = full ? INT_MIN : (p.causal ? 0 : INT_MIN);
+      const int dhi = full ? INT_MAX : (p.window > 0 ? p.window - 1 : INT_MAX);
+      const int kin = (full || kj < L) ? 1 : 0;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qr = 32 * mt + (r >> 2) * 8 + 4 * c + (r & 3);
-          float x = sacc[mt][r] * p.scale_log2 - sm.lse2[qr];
-          if (!full && (kj >= L || !visible(q0 + qr, kj, p.causal, p.window))) x = -INFINITY;
-          const float pv = fast_exp2(x);
-          sacc[mt][r] = pv;
-          pacc[mt][r] = pv * (pacc[mt][r] - sm.delta[qr]) * p.scale;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int qr = 32 * mt + 8 * g4 + 4 * c;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + qr);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt + qr);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g4 + e;
+            const int dd = q0 + qr + e - kj;
+            const int ok = kin & (dd >= dlo) & (dd <= dhi);
+            const float x = ok ? sacc[mt][r] * p.scale_log2 - l4[e] : -INFINITY;
+            const float pv = fast_exp2(x);
+            sacc[mt][r] = pv;
+            pacc[mt][r] = pv * (pacc[mt][r] - d4[e]) * p.scale;
+          }
         }
       }
 
-      // dV += P^T dO and dK += dS^T Q over the 64 queries (four 16-query
-      // steps).  Slot (c, e) of step ks holds query 16 ks + (e / 4) * 8 +
-      // 4 c + e % 4, where the C layout of S keeps it.
+      // -- dV += P^T dO, dK += dS^T Q over the BM queries (16 per step).
+      // Slot (c, e) of step qs holds query 16 qs + (e / 4) * 8 + 4 c + e % 4,
+      // where the C layout of S keeps it; the B operands are read transposed.
 #pragma unroll
-      for (int ks = 0; ks < kBM / 16; ++ks) {
-        const T8 pa = pack8<T>(sacc[ks >> 1], 8 * (ks & 1));
-        const T8 sa = pack8<T>(pacc[ks >> 1], 8 * (ks & 1));
+      for (int qs2 = 0; qs2 < BM / 16; ++qs2) {
+        const int mt = qs2 >> 1, rb = 8 * (qs2 & 1);
+        const T8 pa = pack8<T>(sacc[mt], rb);
+        const T8 sa = pack8<T>(pacc[mt], rb);
+        const int row = 16 * qs2 + 4 * c + (l16 >> 2);
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          const T* dor = &sm.dot[32 * t + n][16 * ks + 4 * c];
-          const T* qr = &sm.qt[32 * t + n][16 * ks + 4 * c];
-          dv[t] = mfma32(pa, cat8<T>(ld8<T>(dor), ld8<T>(dor + 8)), dv[t]);
-          dk[t] = mfma32(sa, cat8<T>(ld8<T>(qr), ld8<T>(qr + 8)), dk[t]);
+        for (int t = 0; t < NT; ++t) {
+          const int col = 32 * t + 16 * g16 + 4 * (lane & 3);
+          const int o0 = rm_off<D>(row, col), o1 = rm_off<D>(row + 8, col);
+          dv[kt][t] = mfma32(pa, tr_pair<T>(dos, o0, o1), dv[kt][t]);
+          dk[kt][t] = mfma32(sa, tr_pair<T>(qs, o0, o1), dk[kt][t]);
         }
       }
 
-      // dS to LDS, query-major, for dQ = dS K.
+      // -- dS to LDS, key-major: 4 consecutive queries per 8-byte write.
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sm.ds[32 * mt + (r >> 2) * 8 + 4 * c + (r & 3)][32 * w + n] = to16<T>(pacc[mt][r]);
-      }
-      __syncthreads();
-
-      // dQ partial = dS K over all 128 keys of the block.
-      f32x16 qacc[kDqTiles];
+        for (int g4 = 0; g4 < 4; ++g4) {
+          T4 v4;
 #pragma unroll
-      for (int t = 0; t < kDqTiles; ++t) qacc[t] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < kBN / 16; ++ks) {
-        const T8 kb = ld16<T>(&sm.kt[32 * dq_nt + n][16 * ks + 8 * c]);
-#pragma unroll
-        for (int t = 0; t < kDqTiles; ++t)
-          qacc[t] = mfma32(ld16<T>(&sm.ds[32 * (dq_mt0 + t) + n][16 * ks + 8 * c]), kb, qacc[t]);
-      }
-      // Region-wide fp32 atomics straight from the C layout.
-      float* dqh = p.dq_accum + (size_t)a * q_stride + (size_t)h * D + 32 * dq_nt + n;
-#pragma unroll
-      for (int t = 0; t < kDqTiles; ++t) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qrow = q0 + 32 * (dq_mt0 + t) + (r >> 2) * 8 + 4 * c + (r & 3);
-          if (qrow < L)
-            __hip_atomic_fetch_add(dqh + (size_t)qrow * q_stride, qacc[t][r], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+          for (int e = 0; e < 4; ++e) v4[e] = to16<T>(pacc[mt][4 * g4 + e]);
+          *reinterpret_cast<u32x2*>(dss + dst_off<BM>(32 * kKT * w + 32 * kt + n, 32 * mt + 8 * g4 + 4 * c)) =
+              __builtin_bit_cast(u32x2, v4);
         }
+    }
+
+    // -- next pair's Q / dO / lse / Delta into the other buffer; loads for
+    //    the pair after it go out before this pair's atomics.
+    if (i + 1 < npairs) store_pair(buf ^ 1);
+    if (i + 2 < npairs) load_pair(i + 2);
+    __syncthreads();
+
+    // -- dQ partial = dS K for this wave's two 16 x 16 tiles over all 256
+    //    keys.  Slot (g, e) of the 16x16x32 operands holds key 32 ks + 8 g + e.
+    f32x4 qacc0 = f32x4{}, qacc1 = f32x4{};
+    {
+      const int qcol = 16 * dq_qt + 4 * (lane & 3);
+      const int dcol = 16 * dq_dt + 4 * (lane & 3);
+#pragma unroll 2
+      for (int ks = 0; ks < kBN / 32; ++ks) {
+        const int key = 32 * ks + 8 * g64 + (l16 >> 2);
+        const T8 as = tr_pair<T>(dss, dst_off<BM>(key, qcol), dst_off<BM>(key + 4, qcol));
+        const T8 b0 = tr_pair<T>(smem, C::K_OFF + rm_off<D>(key, dcol),
+                                 C::K_OFF + rm_off<D>(key + 4, dcol));
+        const T8 b1 = tr_pair<T>(smem, C::K_OFF + rm_off<D>(key, dcol + 16),
+                                 C::K_OFF + rm_off<D>(key + 4, dcol + 16));
+        qacc0 = mfma16(as, b0, qacc0);
+        qacc1 = mfma16(as, b1, qacc1);
+      }
+    }
+    // -- region-wide fp32 atomics straight from the C layout; rows past the
+    //    sequence end fall outside the resource and are dropped.
+    {
+      const int rows = min(L - q0, BM);
+      const rsrc_t dq = make_rsrc(p.dq_accum + ((size_t)(a + q0) * p.hq + h) * D, rows * q_row * 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        buf_atomic_add(dq, dq_lane_off + r * q_row * 4, qacc0[r]);
+        buf_atomic_add(dq, dq_lane_off + r * q_row * 4 + 64, qacc1[r]);
       }
     }
   }
 
-  // Single write of dK and dV (C layout: column = dim, row = key).
-  T* dkp = static_cast<T*>(p.dk) + (size_t)a * kv_stride + (size_t)g * D;
-  T* dvp = static_cast<T*>(p.dv) + (size_t)a * kv_stride + (size_t)g * D;
+  // ---- single write of dK and dV (C layout: column = dim, row = key) -------
+  const rsrc_t dkr = make_rsrc(static_cast<T*>(p.dk) + kv_base, nkeys * kv_row * 2);
+  const rsrc_t dvr = make_rsrc(static_cast<T*>(p.dv) + kv_base, nkeys * kv_row * 2);
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
+  for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int j = kv0 + 32 * w + (r >> 2) * 8 + 4 * c + (r & 3);
-      if (j < L) {
-        const size_t off = (size_t)j * kv_stride + 32 * t + n;
-        dkp[off] = to16<T>(dk[t][r]);
-        dvp[off] = to16<T>(dv[t][r]);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t row = 32 * kKT * w + 32 * kt + (r >> 2) * 8 + 4 * c + (r & 3);
+        const uint32_t off = (row * kv_row + 32 * t + n) * 2;
+        buf_store_b16(dkr, off, bits16(to16<T>(dk[kt][t][r])));
+        buf_store_b16(dvr, off, bits16(to16<T>(dv[kt][t][r])));
       }
-    }
-  }
 }
 
 template <typename T, int D>
 hipError_t bwd_t(const BwdArgs& args, int nkb, hipStream_t stream) {
   const unsigned blocks = (unsigned)nkb * args.num_seqs * args.hkv;
-  hipLaunchKernelGGL((bwd_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, args);
+  hipLaunchKernelGGL((bwd_kernel<T, D>), dim3(blocks), dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 

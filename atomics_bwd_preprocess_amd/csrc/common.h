@@ -39,6 +39,16 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// MFMA 16x16x32 (v_mfma_f32_16x16x32_{f16,bf16}): lane l, g = l / 16, i = l % 16:
+//   A (16 x 32): row i, k-slots (g, e); B (32 x 16): column i, k-slots (g, e);
+//   C (16 x 16): register r = 0..3 holds row 4 g + r, column i.
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Round-to-nearest-even conversion of fp32 to the 16-bit storage type.
 template <typename T> __device__ __forceinline__ T to16(float x) { return static_cast<T>(x); }
 
@@ -90,6 +100,33 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 // Value held by lane (l ^ 32).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Raw buffer resources (gfx9 descriptor: stride 0, num_records in bytes).
+// Loads beyond num_records return zero and stores / atomics beyond it are
+// dropped by the hardware, which is how the kernels handle tile tails.  The
+// whole offset is passed in the VGPR operand (soffset = 0).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store_b16(rsrc_t r, uint32_t off, unsigned short v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_atomic_add(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, off, 0, 0);
+}
+template <typename T> __device__ __forceinline__ unsigned short bits16(T x) {
+  return __builtin_bit_cast(unsigned short, x);
+}
 
 // Sequence bounds [a, b) clamped to [0, total]; cu == nullptr means a dense batch.
 __device__ __forceinline__ void seq_bounds(const int32_t* cu, int s, int max_seqlen, int total,
