@@ -193,7 +193,7 @@ def attn_bwd_preprocess(shape: Shape, o, dout, lse, cu_seqlens, sink, delta, dq_
 
 def attn_bwd(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dq_accum, dk, dv,
              stream=None) -> None:
-    """Main backward: accumulates dQ into dq_accum (atomics) and writes dk, dv."""
+    """Main backward: accumulates dQ / scale into dq_accum (atomics), writes dk, dv."""
     import torch
 
     T, Hq, Hkv, D, dt = _dims(shape)
@@ -212,7 +212,7 @@ def attn_bwd(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dq_accum, dk, 
 
 
 def attn_bwd_postprocess(shape: Shape, dq_accum, dq, stream=None) -> None:
-    """dq = RNE cast of the fp32 dq_accum."""
+    """dq = RNE cast of scale * dq_accum (fp32 multiply; dq_accum holds dQ / scale)."""
     import torch
 
     T, Hq, Hkv, D, dt = _dims(shape)

@@ -131,6 +131,10 @@ __device__ __forceinline__ typename V8<T>::type tr_pair(const char* smem, int of
   return __builtin_bit_cast(typename V8<T>::type, r);
 }
 
+// Wave-uniform integer kept in a scalar register (buffer descriptor fields
+// must be scalar; clamps otherwise tend to land in vector registers).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 template <typename T>
 __device__ __forceinline__ typename V8<T>::type lds16(const char* smem, int off) {
   return __builtin_bit_cast(typename V8<T>::type, *reinterpret_cast<const u32x4*>(smem + off));
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   const int G = p.hq / p.hkv;
   const uint32_t kv_row = (uint32_t)p.hkv * D;  // elements between key rows
   const uint32_t q_row = (uint32_t)p.hq * D;    // elements between query rows
-  const int nkeys = min(L - kv0, kBN);          // valid keys of this block
+  const int nkeys = uni(min(L - kv0, kBN));     // valid keys of this block
 
   // Buffer resources over this block's keys: rows past the sequence end read
   // as zero and their stores are dropped.
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   auto load_pair = [&](int i) {
     const int h = g * G + i / nq;
     const int q0 = (ib0 + i % nq) * BM;
-    const int rows = max(0, min(L - q0, BM));
+    const int rows = uni(min(L - q0, BM));  // >= 1: query blocks start inside the sequence
     const size_t qb = ((size_t)(a + q0) * p.hq + h) * D;
     const rsrc_t qr = make_rsrc(static_cast<const T*>(p.q) + qb, rows * q_row * 2);
     const rsrc_t dr = make_rsrc(static_cast<const T*>(p.dout) + qb, rows * q_row * 2);
@@ -307,14 +311,16 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
         }
       }
 
-      // -- P = exp2(S scale log2e - lse log2e); dS = P (dP - Delta) scale
+      // -- P = exp2(S scale log2e - lse log2e); dS' = P (dP - Delta).  The
+      //    factor `scale` of dS is applied once to dK (epilogue) and to dQ
+      //    (postprocess), not per element.  Masks only on tiles that need them:
+      //    visible iff lo <= q - k <= hi and k < L.
       const bool full = (q0 + BM <= L) && (tk_hi < L) && (!p.causal || tk_hi <= q0) &&
                         (p.window <= 0 || tk_lo > q0 + BM - 1 - p.window);
-      // Visible iff lo <= q - k <= hi and k < L (branch-free per element).
       const int kj = tk_lo + n;
-      const int dlo = full ? INT_MIN : (p.causal ? 0 : INT_MIN);
-      const int dhi = full ? INT_MAX : (p.window > 0 ? p.window - 1 : INT_MAX);
-      const int kin = (full || kj < L) ? 1 : 0;
+      const int dlo = p.causal ? 0 : INT_MIN;
+      const int dhi = p.window > 0 ? p.window - 1 : INT_MAX;
+      const int kin = kj < L ? 1 : 0;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -325,12 +331,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g4 + e;
-            const int dd = q0 + qr + e - kj;
-            const int ok = kin & (dd >= dlo) & (dd <= dhi);
-            const float x = ok ? sacc[mt][r] * p.scale_log2 - l4[e] : -INFINITY;
+            float x = sacc[mt][r] * p.scale_log2 - l4[e];
+            if (!full) {
+              const int dd = q0 + qr + e - kj;
+              x = (kin & (dd >= dlo) & (dd <= dhi)) ? x : -INFINITY;
+            }
             const float pv = fast_exp2(x);
             sacc[mt][r] = pv;
-            pacc[mt][r] = pv * (pacc[mt][r] - d4[e]) * p.scale;
+            pacc[mt][r] = pv * (pacc[mt][r] - d4[e]);
           }
         }
       }
@@ -393,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     // -- region-wide fp32 atomics straight from the C layout; rows past the
     //    sequence end fall outside the resource and are dropped.
     {
-      const int rows = min(L - q0, BM);
+      const int rows = uni(min(L - q0, BM));
       const rsrc_t dq = make_rsrc(p.dq_accum + ((size_t)(a + q0) * p.hq + h) * D, rows * q_row * 4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -414,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
       for (int r = 0; r < 16; ++r) {
         const uint32_t row = 32 * kKT * w + 32 * kt + (r >> 2) * 8 + 4 * c + (r & 3);
         const uint32_t off = (row * kv_row + 32 * t + n) * 2;
-        buf_store_b16(dkr, off, bits16(to16<T>(dk[kt][t][r])));
+        buf_store_b16(dkr, off, bits16(to16<T>(dk[kt][t][r] * p.scale)));
         buf_store_b16(dvr, off, bits16(to16<T>(dv[kt][t][r])));
       }
 }

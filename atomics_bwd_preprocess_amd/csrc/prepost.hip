@@ -6,7 +6,8 @@
 //    kernel): Delta = row sum of O * dO in fp32, zeroing of the fp32 dQ
 //    accumulator, and dsink = -sum_t exp(sink - lse) * Delta.
 //  * postprocess (same PR: the postprocess kernel that casts the fp32
-//    accumulated gradient to fp16): dQ = RNE cast of the fp32 accumulator.
+//    accumulated gradient to fp16): dQ = RNE cast of scale x the fp32
+//    accumulator (the main pass leaves the score scale out of dS).
 //
 // Algorithmic bytes (e = 2 bytes per 16-bit element, R = T * Hq rows):
 //   delta kernel:  R * D * 2e (O, dO) + R * 4 (Delta) + R * D * 4 (zeroing)
@@ -74,10 +75,11 @@ __global__ __launch_bounds__(256) void dsink_kernel(const float* __restrict__ ls
   if (threadIdx.x == 0) dsink[h] = -((part[0] + part[1]) + (part[2] + part[3]));
 }
 
-// dq[i] = RNE(dq_accum[i]) for 8 consecutive elements per thread.
+// dq[i] = RNE(scale * dq_accum[i]) for 8 consecutive elements per thread
+// (the main pass accumulates dS' K with dS' = dS / scale).
 template <typename T>
 __global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ src,
-                                                   T* __restrict__ dst, size_t n8) {
+                                                   T* __restrict__ dst, size_t n8, float scale) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
   const f32x4 a = *reinterpret_cast<const f32x4*>(src + 8 * i);
@@ -85,8 +87,8 @@ __global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ src
   typename V8<T>::type r;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    r[k] = to16<T>(a[k]);
-    r[k + 4] = to16<T>(b[k]);
+    r[k] = to16<T>(a[k] * scale);
+    r[k + 4] = to16<T>(b[k] * scale);
   }
   st16<T>(dst + 8 * i, r);
 }
@@ -125,10 +127,10 @@ hipError_t launch_postprocess(const Problem& p, const float* dq_accum, void* dq,
   const dim3 grid((unsigned)((n8 + 255) / 256));
   if (p.bf16)
     hipLaunchKernelGGL(cast_kernel<__bf16>, grid, dim3(256), 0, stream, dq_accum,
-                       static_cast<__bf16*>(dq), n8);
+                       static_cast<__bf16*>(dq), n8, p.scale);
   else
     hipLaunchKernelGGL(cast_kernel<_Float16>, grid, dim3(256), 0, stream, dq_accum,
-                       static_cast<_Float16*>(dq), n8);
+                       static_cast<_Float16*>(dq), n8, p.scale);
   return hipGetLastError();
 }
 

@@ -115,10 +115,11 @@ attn_status_t attn_bwd_preprocess(const attn_shape_t* shape, const void* o, cons
  * tile, then dV = P^T dO, dP = dO V^T, dS = P o (dP - Delta) * scale,
  * dK = dS^T Q and dQ = dS K ([ASC] review thread, kernels k1-k5 fused;
  * spec formulas).
- *  - dq_accum (zeroed by attn_bwd_preprocess) receives dQ through fp32
- *    atomic adds issued once per (query tile, key tile) as one coalesced
- *    region-wide sweep ([TL] regional atomic add; [TRI] atomics issued from
- *    the matrix-core layout).  Summation order varies run to run.
+ *  - dq_accum (zeroed by attn_bwd_preprocess) receives dQ / scale through
+ *    fp32 atomic adds issued once per (query tile, key tile) as one
+ *    coalesced region-wide sweep ([TL] regional atomic add; [TRI] atomics
+ *    issued from the matrix-core layout).  The score scale is applied by
+ *    attn_bwd_postprocess.  Summation order varies run to run.
  *  - dk, dv are WRITTEN once per key row after accumulating, in fp32
  *    registers, over every query block and every query head of the group
  *    ([TL] review: accumulate locally, write once).  They are deterministic.
@@ -131,7 +132,8 @@ attn_status_t attn_bwd(const attn_shape_t* shape, const void* q, const void* k, 
 
 /*
  * Backward postprocess ([ASC] postprocess kernel casting the fp32 gradient
- * accumulator): dq[t][h][d] = RNE cast of dq_accum[t][h][d] to the storage dtype.
+ * accumulator): dq[t][h][d] = RNE cast of (scale * dq_accum[t][h][d]) to the
+ * storage dtype, the multiplication done in fp32.
  */
 attn_status_t attn_bwd_postprocess(const attn_shape_t* shape, const float* dq_accum, void* dq,
                                    hipStream_t stream);
