@@ -36,7 +36,7 @@
 // i, so they never queue behind them.  Transposed operands (dO, Q for
 // dV / dK; dS, K for dQ) come from gfx950's transposing LDS read, and dS is
 // stored key-major with 8-byte writes.  All LDS patterns are bank-conflict
-// free (the swizzles are modelled by the host tests of the LDS layout).
+// free under the measured bank model (see the swizzle notes below).
 // One workgroup barrier per pair.
 //
 // The sink needs no term here: it only enters through lse.
@@ -97,18 +97,31 @@ struct BwdArgs {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Row-major tiles: 16-byte chunk c of row r lives at chunk
-// (c & ~7) | ((c & 7) ^ chunk_swz(r)).
-__device__ __forceinline__ int chunk_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// LDS bank model (measured on MI355X): 64 banks of 4 bytes; 16-byte accesses
+// resolve in passes of 16 lanes, 8-byte and transposing accesses in passes of
+// 32 lanes.  The swizzles below make every access pattern of this kernel
+// conflict-free under that model (checked exhaustively by the host model of
+// the LDS layout in the tests).
+//
+// Row-major tiles (D columns): 16-byte chunk c of row r lives at chunk
+// c ^ chunk_swz(r): 16 consecutive rows hit 16 distinct chunks (16-byte operand
+// reads), and 4 consecutive rows spread a 64-byte column block over the whole
+// bank range (transposing reads).
+template <int D>
+__device__ __forceinline__ int chunk_swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 template <int D>
 __device__ __forceinline__ int rm_off(int r, int col) {  // col: multiple of 4
-  const int c = col >> 3;
-  return r * (D * 2) + (((c & ~7) | ((c & 7) ^ chunk_swz(r))) << 4) + ((col & 7) << 1);
+  return r * (D * 2) + (((col >> 3) ^ chunk_swz<D>(r)) << 4) + ((col & 7) << 1);
 }
-// Key-major dS tile: 8-byte slot s of row r lives at slot s ^ slot_swz(r).
+// Key-major dS tile (BM queries per row): 8-byte slot s of row r lives at
+// slot s ^ slot_swz(r).
 template <int BM>
 __device__ __forceinline__ int slot_swz(int r) {
-  return BM == 32 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
+  return BM == 32 ? ((((r >> 3) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 4) & 1))
+                  : ((((r >> 3) & 1) << 3) | (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) |
+                     ((r >> 4) & 1));
 }
 template <int BM>
 __device__ __forceinline__ int dst_off(int r, int q) {  // q: multiple of 4

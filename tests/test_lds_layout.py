@@ -1,37 +1,42 @@
 """Host model of the main backward kernel's LDS layouts.
 
 The kernel stores row-major tiles (K, Q, dO) with 16-byte chunks XOR-swizzled
-inside each 128-byte half-row, and the transposed dS tile with 8-byte slots
-XOR-swizzled inside each row.  These tests recompute, for every access
-pattern the kernel issues, which 4-byte banks each group of lanes touches
-(32 banks; 16-byte reads in groups of 8 lanes, 8-byte reads / writes and
-transposing reads in groups of 16 lanes) and check that (a) the swizzle is a
-bijection and (b) no two lanes of a group touch the same bank.
+within each row, and the transposed dS tile with 8-byte slots XOR-swizzled
+within each row.  These tests recompute, for every access pattern the kernel
+issues, how many extra cycles bank conflicts cost, and require zero.
 
-The formulas mirror ``chunk_swz`` / ``slot_swz`` in csrc/bwd.hip.
+Bank model (established on MI355X with a microbenchmark of isolated access
+patterns and the SQ_LDS_BANK_CONFLICT counter, which it reproduces exactly):
+64 banks of 4 bytes; 16-byte accesses are resolved in passes of 16 lanes,
+8-byte accesses and transposing reads (ds_read_b64_tr_b16) in passes of 32
+lanes; a pass costs one extra cycle per additional distinct dword mapped to
+its busiest bank.  The formulas below mirror chunk_swz / slot_swz in
+csrc/bwd.hip.
 """
 import itertools
+from collections import defaultdict
 
 import pytest
 
-BANKS = 32
+BANKS = 64
 
 
-def chunk_swz(r):
-    return ((r & 3) << 1) | ((r >> 2) & 1)
+def chunk_swz(r, d):
+    if d == 128:
+        return ((r & 3) << 2) | ((r >> 2) & 3)
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3)
 
 
 def rm_byte(r, col, d):
     """Byte offset of 16-bit element (r, col) in a swizzled row-major tile of d columns."""
     chunk, within = divmod(col, 8)
-    phys = (chunk & ~7) | ((chunk & 7) ^ chunk_swz(r))
-    return r * d * 2 + phys * 16 + within * 2
+    return r * d * 2 + (chunk ^ chunk_swz(r, d)) * 16 + within * 2
 
 
 def slot_swz(r, bm):
     if bm == 32:
-        return (((r >> 1) & 1) << 2) | ((r >> 2) & 3)
-    return ((r & 3) << 2) | ((r >> 2) & 3)
+        return (((r >> 3) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 4) & 1)
+    return (((r >> 3) & 1) << 3) | (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 4) & 1)
 
 
 def dst_byte(r, q, bm):
@@ -40,80 +45,103 @@ def dst_byte(r, q, bm):
     return r * bm * 2 + (slot ^ slot_swz(r, bm)) * 8 + within * 2
 
 
-def banks(byte, nbytes):
-    assert byte % 4 == 0
-    return {((byte // 4) + k) % BANKS for k in range(nbytes // 4)}
+def extra_cycles(addrs, nbytes):
+    hit = defaultdict(set)
+    for a in addrs:
+        assert a % 4 == 0
+        for k in range(nbytes // 4):
+            dw = a // 4 + k
+            hit[dw % BANKS].add(dw)
+    return max(len(v) for v in hit.values()) - 1
 
 
-def conflict_free(addresses, nbytes):
-    seen = set()
-    for a in addresses:
-        b = banks(a, nbytes)
-        if seen & b:
-            return False
-        seen |= b
-    return True
+def instr_conflicts(addrs, nbytes):
+    lanes = 16 if nbytes == 16 else 32
+    return sum(extra_cycles(addrs[i:i + lanes], nbytes) for i in range(0, 64, lanes))
 
 
-def tr_lane_address(l, k_base, col_base, c_stride=8):
-    """Row and column addressed by lane l of a transposing 4x16 read: lanes
-    of each 16-lane group address rows k0 + p/4 and 4-element column pieces
-    n0 + 4 (p % 4); k0 = k_base + c_stride * (l / 32),
-    n0 = col_base + 16 * ((l / 16) % 2)."""
+def tr32(l, k_base, col_base, c_stride):
+    """Row/column addressed by lane l for a transposed 32x32x16 MFMA operand:
+    rows k0 + p/4 with k0 = k_base + c_stride * (l / 32), columns
+    n0 + 4 (p % 4) with n0 = col_base + 16 * ((l / 16) % 2), p = l % 16."""
     p = l % 16
-    return (k_base + c_stride * (l // 32) + p // 4,
-            col_base + 16 * ((l // 16) % 2) + 4 * (p % 4))
+    return k_base + c_stride * (l // 32) + p // 4, col_base + 16 * ((l // 16) % 2) + 4 * (p % 4)
 
 
-@pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("rows", [32, 64, 256])
-def test_row_major_swizzle_is_bijective(d, rows):
-    offs = {rm_byte(r, c, d) for r in range(rows) for c in range(0, d, 8)}
-    assert len(offs) == rows * d // 8
-    assert max(offs) < rows * d * 2 and all(o % 16 == 0 for o in offs)
+def tr16(l, k_base, col_base):
+    """Same for a 16x16x32 operand: lane group g = l / 16 holds k-slots
+    8 g .. 8 g + 7, so rows k_base + 8 g + p/4, columns col_base + 4 (p % 4)."""
+    p = l % 16
+    return k_base + 8 * (l // 16) + p // 4, col_base + 4 * (p % 4)
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_row_major_b128_reads(d):
-    # MFMA A/B operand loads: lane l reads row (base + l % 32), chunk (2 ks + l / 32).
-    for base, ks in itertools.product(range(0, 256, 32), range(d // 16)):
-        addrs = [rm_byte(base + l % 32, 8 * (2 * ks + l // 32), d) for l in range(64)]
-        for g in range(8):
-            assert conflict_free(addrs[8 * g:8 * g + 8], 16), (base, ks, g)
+CFG = [(128, 32), (64, 64)]  # (D, BM)
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_row_major_chunk_writes(d):
-    # Staging stores: thread t writes row t / (d / 8), chunk t % (d / 8).
-    ch = d // 8
-    for t0 in range(0, 256, 64):
-        addrs = [rm_byte((t0 + l) // ch, 8 * ((t0 + l) % ch), d) for l in range(64)]
-        for g in range(8):
-            assert conflict_free(addrs[8 * g:8 * g + 8], 16)
+def test_model_reproduces_measured_conflicts():
+    """The previous swizzle measured 4 extra cycles per K b128 read and 2 per
+    transposing read; unswizzled 256-byte rows measured 6 and linear reads 0."""
+    old = lambda r: ((r & 3) << 1) | ((r >> 2) & 1)  # noqa: E731
+
+    def old_rm(r, col):
+        c = col >> 3
+        return r * 256 + (((c & ~7) | ((c & 7) ^ old(r))) << 4) + ((col & 7) << 1)
+
+    assert instr_conflicts([old_rm(l % 32, 8 * (l // 32)) for l in range(64)], 16) == 4
+    assert instr_conflicts([old_rm(*tr32(l, 0, 0, 4)) for l in range(64)], 8) == 2
+    assert instr_conflicts([(lambda r, c: r * 256 + 2 * c)(*tr32(l, 0, 0, 4)) for l in range(64)], 8) == 6
+    assert instr_conflicts([8 * l for l in range(64)], 8) == 0
 
 
-@pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("c_stride", [4, 8])
-def test_row_major_transposing_reads(d, c_stride):
-    # Q / dO (c_stride 4) and K (c_stride 8) as transposed MFMA operands:
-    # k rows from k_base, columns of a 32-wide tile.
-    for k_base, col in itertools.product(range(0, 64, 4), range(0, d, 32)):
-        addrs = [rm_byte(*tr_lane_address(l, k_base, col, c_stride), d) for l in range(64)]
-        for g in range(4):
-            assert conflict_free(addrs[16 * g:16 * g + 16], 8), (k_base, col, g)
-
-
-@pytest.mark.parametrize("bm", [32, 64])
-def test_transposed_ds_layout(bm):
+@pytest.mark.parametrize("d,bm", CFG)
+def test_swizzles_are_bijections(d, bm):
+    offs = {rm_byte(r, c, d) for r in range(256) for c in range(0, d, 8)}
+    assert len(offs) == 256 * d // 8 and max(offs) < 256 * d * 2
     offs = {dst_byte(r, q, bm) for r in range(256) for q in range(0, bm, 4)}
     assert len(offs) == 256 * bm // 4 and max(offs) < 256 * bm * 2
-    # writes: lane l (key 32 kt + l % 32) writes 4 queries at q = 32 mt + 8 g + 4 (l / 32)
-    for kt, mt, g in itertools.product(range(8), range(bm // 32), range(4)):
-        addrs = [dst_byte(32 * kt + l % 32, 32 * mt + 8 * g + 4 * (l // 32), bm) for l in range(64)]
-        for grp in range(4):
-            assert conflict_free(addrs[16 * grp:16 * grp + 16], 8), (kt, mt, g, grp)
-    # transposing reads: rows = keys (k_base + ...), columns = queries of tile mt
-    for k_base, mt in itertools.product(range(0, 256, 4), range(bm // 32)):
-        addrs = [dst_byte(*tr_lane_address(l, k_base, 32 * mt), bm) for l in range(64)]
-        for grp in range(4):
-            assert conflict_free(addrs[16 * grp:16 * grp + 16], 8), (k_base, mt, grp)
+
+
+@pytest.mark.parametrize("d,bm", CFG)
+def test_b128_operand_reads(d, bm):
+    # Q / dO rows (A operand of S, dP) and K rows (B operand of S): lane l reads
+    # row base + l % 32, chunk 2 ks + l / 32.
+    for base, ks in itertools.product(range(0, 256, 32), range(d // 16)):
+        a = [rm_byte(base + l % 32, 8 * (2 * ks + l // 32), d) for l in range(64)]
+        assert instr_conflicts(a, 16) == 0, (base, ks)
+
+
+@pytest.mark.parametrize("d,bm", CFG)
+def test_b128_staging_writes(d, bm):
+    # staging stores: thread t writes row t / (d / 8), chunk t % (d / 8)
+    ch = d // 8
+    for t0 in range(0, 256 * ch, 64):
+        a = [rm_byte((t0 + l) // ch, 8 * ((t0 + l) % ch), d) for l in range(64)]
+        assert instr_conflicts(a, 16) == 0, t0
+
+
+@pytest.mark.parametrize("d,bm", CFG)
+def test_transposing_reads_of_q_and_do(d, bm):
+    # B operand of dV / dK: rows 16 qs + 4 c + p/4 (and + 8), columns of dim tile t
+    for qs, t, half in itertools.product(range(bm // 16), range(d // 32), (0, 8)):
+        a = [rm_byte(*tr32(l, 16 * qs + half, 32 * t, 4), d) for l in range(64)]
+        assert instr_conflicts(a, 8) == 0, (qs, t, half)
+
+
+@pytest.mark.parametrize("d,bm", CFG)
+def test_transposing_reads_of_k(d, bm):
+    # B operand of dQ (16x16x32): rows 32 ks + 8 g + p/4 (and + 4), dim tile dt
+    for ks, dt, half in itertools.product(range(8), range(d // 16), (0, 4)):
+        a = [rm_byte(*tr16(l, 32 * ks + half, 16 * dt), d) for l in range(64)]
+        assert instr_conflicts(a, 8) == 0, (ks, dt, half)
+
+
+@pytest.mark.parametrize("d,bm", CFG)
+def test_transposed_ds_writes_and_reads(d, bm):
+    # writes: lane l (key 32 w + l % 32) stores 4 queries at q = 32 mt + 8 g + 4 (l / 32)
+    for w, mt, g in itertools.product(range(8), range(bm // 32), range(4)):
+        a = [dst_byte(32 * w + l % 32, 32 * mt + 8 * g + 4 * (l // 32), bm) for l in range(64)]
+        assert instr_conflicts(a, 8) == 0, (w, mt, g)
+    # transposing reads (A operand of dQ, 16x16x32): rows = keys, columns = query tile qt
+    for ks, qt, half in itertools.product(range(8), range(bm // 16), (0, 4)):
+        a = [dst_byte(*tr16(l, 32 * ks + half, 16 * qt), bm) for l in range(64)]
+        assert instr_conflicts(a, 8) == 0, (ks, qt, half)
