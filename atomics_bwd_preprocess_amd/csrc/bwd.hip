@@ -153,7 +153,9 @@ __device__ __forceinline__ typename V8<T>::type lds16(const char* smem, int off)
   return __builtin_bit_cast(typename V8<T>::type, *reinterpret_cast<const u32x4*>(smem + off));
 }
 
-template <typename T, int D>
+// WIN: sliding-window problems, where most key tiles of a query block are
+// invisible; the dQ product then runs only over the visible key tiles.
+template <typename T, int D, bool WIN>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   using C = Cfg<D>;
   using T8 = typename V8<T>::type;
@@ -294,12 +296,17 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
       const bool empty = tk_lo >= L || q0 >= L || (p.causal && tk_lo > q0 + BM - 1) ||
                          (p.window > 0 && tk_hi <= q0 - p.window);
       if (empty) {
-        const u32x2 z = {0u, 0u};
+        // With WIN the dQ product below skips exactly the key tiles that no
+        // query of the block can see, so their dS rows are never read;
+        // otherwise they are zeroed.
+        if constexpr (!WIN) {
+          const u32x2 z = {0u, 0u};
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4)
-            *reinterpret_cast<u32x2*>(dss + dst_off<BM>(32 * kKT * w + 32 * kt + n, 32 * mt + 8 * g4 + 4 * c)) = z;
+            for (int g4 = 0; g4 < 4; ++g4)
+              *reinterpret_cast<u32x2*>(dss + dst_off<BM>(32 * kKT * w + 32 * kt + n, 32 * mt + 8 * g4 + 4 * c)) = z;
+        }
         continue;
       }
       // -- S = Q K^T and dP = dO V^T: [BM queries] x [32 keys]
@@ -393,14 +400,24 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     if (i + 2 < npairs) load_pair(i + 2);
     __syncthreads();
 
-    // -- dQ partial = dS K for this wave's two 16 x 16 tiles over all 256
-    //    keys.  Slot (g, e) of the 16x16x32 operands holds key 32 ks + 8 g + e.
+    // -- dQ partial = dS K for this wave's two 16 x 16 tiles.  Slot (g, e)
+    //    of the 16x16x32 operands holds key 32 ks + 8 g + e; k-step ks covers
+    //    the keys of wave ks.  With WIN only the key tiles some query of the
+    //    block can see are visited (exactly the tiles not "empty" above).
     f32x4 qacc0 = f32x4{}, qacc1 = f32x4{};
     {
+      int ks_lo = 0, ks_hi = kBN / 32;
+      if constexpr (WIN) {
+        ks_hi = min(ks_hi, (nkeys + 31) / 32);
+        ks_hi = min(ks_hi, (q0 + BM - 1 - kv0) / 32 + 1);  // windows are causal
+        // tile ks is visible iff 32 ks + 31 > q0 - W - kv0, i.e.
+        // ks >= floor((q0 - W + 1 - kv0) / 32) (arithmetic shift = floor).
+        ks_lo = max(0, (q0 - p.window + 1 - kv0) >> 5);
+      }
       const int qcol = 16 * dq_qt + 4 * (lane & 3);
       const int dcol = 16 * dq_dt + 4 * (lane & 3);
 #pragma unroll 2
-      for (int ks = 0; ks < kBN / 32; ++ks) {
+      for (int ks = ks_lo; ks < ks_hi; ++ks) {
         const int key = 32 * ks + 8 * g64 + (l16 >> 2);
         const T8 as = tr_pair<T>(dss, dst_off<BM>(key, qcol), dst_off<BM>(key + 4, qcol));
         const T8 b0 = tr_pair<T>(smem, C::K_OFF + rm_off<D>(key, dcol),
@@ -443,7 +460,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
 template <typename T, int D>
 hipError_t bwd_t(const BwdArgs& args, int nkb, hipStream_t stream) {
   const unsigned blocks = (unsigned)nkb * args.num_seqs * args.hkv;
-  hipLaunchKernelGGL((bwd_kernel<T, D>), dim3(blocks), dim3(kThreads), 0, stream, args);
+  if (args.window > 0)
+    hipLaunchKernelGGL((bwd_kernel<T, D, true>), dim3(blocks), dim3(kThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((bwd_kernel<T, D, false>), dim3(blocks), dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 
