@@ -232,6 +232,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   // Prefetch registers: PF chunks of Q and of dO per thread, plus lse / Delta.
   u32x4 pq[C::PF], pdo[C::PF];
   float plse = 0.0f, pdlt = 0.0f;
+  int prows = 0;
   auto load_pair = [&](int i) {
     const int h = g * G + i / nq;
     const int q0 = (ib0 + i % nq) * BM;
@@ -246,12 +247,15 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
       pq[u] = buf_load16(qr, off);
       pdo[u] = buf_load16(dr, off);
     }
-    if (tid < BM) {
+    // lse / Delta of the pair's rows; every thread issues the loads (threads
+    // past the block read out of range, i.e. zero) so the number of
+    // outstanding memory operations is the same in every lane.
+    {
       const size_t idx = (size_t)h * p.total + a + q0;
-      const float l = buf_load_f32(make_rsrc(p.lse + idx, rows * 4), tid * 4);
-      pdlt = buf_load_f32(make_rsrc(p.delta + idx, rows * 4), tid * 4);
-      // rows outside the sequence (or that saw nothing) get P = 0
-      plse = (tid >= rows || l == -INFINITY) ? INFINITY : l * kLog2e;
+      const uint32_t off = (uint32_t)(tid & (BM - 1)) * 4 + (tid < BM ? 0u : 0x40000000u);
+      plse = buf_load_f32(make_rsrc(p.lse + idx, rows * 4), off);
+      pdlt = buf_load_f32(make_rsrc(p.delta + idx, rows * 4), off);
+      prows = rows;
     }
   };
   auto store_pair = [&](int buf) {
@@ -263,7 +267,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
       *reinterpret_cast<u32x4*>(smem + C::DO_OFF + buf * C::QT + o) = pdo[u];
     }
     if (tid < BM) {
-      reinterpret_cast<float*>(smem + C::LSE_OFF)[buf * BM + tid] = plse;
+      // rows outside the sequence (or that saw nothing) get P = 0
+      const float l2 = (tid >= prows || plse == -INFINITY) ? INFINITY : plse * kLog2e;
+      reinterpret_cast<float*>(smem + C::LSE_OFF)[buf * BM + tid] = l2;
       reinterpret_cast<float*>(smem + C::DLT_OFF)[buf * BM + tid] = pdlt;
     }
   };
