@@ -357,16 +357,27 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g4 + e;
-            float x = sacc[mt][r] * p.scale_log2 - l4[e];
-            if (!full) {
-              const int dd = q0 + qr + e - kj;
-              x = (kin & (dd >= dlo) & (dd <= dhi)) ? x : -INFINITY;
-            }
-            const float pv = fast_exp2(x);
+            const float pv = fast_exp2(sacc[mt][r] * p.scale_log2 - l4[e]);
             sacc[mt][r] = pv;
             pacc[mt][r] = pv * (pacc[mt][r] - d4[e]);
           }
         }
+      }
+      // Edge tiles: zero P and dS where the key is hidden.  Selecting (not
+      // multiplying) discards whatever the unmasked exponent produced there.
+      // The empty asm keeps this a real branch: if-converted, its compares
+      // and selects would run on every tile.
+      if (!full) {
+        asm volatile("");
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int dd = q0 + 32 * mt + 8 * (r >> 2) + 4 * c + (r & 3) - kj;
+            const bool vis = kin & (dd >= dlo) & (dd <= dhi);
+            sacc[mt][r] = vis ? sacc[mt][r] : 0.0f;
+            pacc[mt][r] = vis ? pacc[mt][r] : 0.0f;
+          }
       }
 
       // -- dV += P^T dO, dK += dS^T Q over the BM queries (16 per step).
