@@ -31,9 +31,11 @@
 // Data movement.  K is staged once into LDS (needed as the dQ operand); V
 // (and K for D = 64) of the wave live in registers as MFMA B operands.
 // Q / dO tiles of a pair (row-major, XOR-swizzled 16-byte chunks) and their
-// lse / Delta rows are double-buffered in LDS and prefetched through
-// registers: the loads for pair i + 2 are issued before the atomics of pair
-// i, so they never queue behind them.  Transposed operands (dO, Q for
+// lse / Delta rows are double-buffered in LDS.  Right after pair i's barrier
+// the Q / dO tiles of pair i + 2 are copied from memory straight into the
+// buffer pair i has released (buffer loads with an LDS destination, so no
+// registers are held for them); lse / Delta pass through registers.  Both go
+// out before the atomics of pair i, so they never queue behind them.  Transposed operands (dO, Q for
 // dV / dK; dS, K for dQ) come from gfx950's transposing LDS read, and dS is
 // stored key-major with 8-byte writes.  All LDS patterns are bank-conflict
 // free under the measured bank model (see the swizzle notes below).
@@ -144,6 +146,31 @@ __device__ __forceinline__ typename V8<T>::type tr_pair(const char* smem, int of
   return __builtin_bit_cast(typename V8<T>::type, r);
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane l writes bytes
+// [16 l, 16 l + 16) after the wave-uniform LDS address `dst`.  Issued as
+// inline assembly so the compiler's wait-count bookkeeping does not follow
+// it (it would otherwise wait for the load before the next LDS access);
+// the kernel waits for it explicitly before the barrier that publishes it.
+// M0 (which supplies the LDS address) is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(rsrc_t r, char* dst, uint32_t off) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(off), "s"(r)
+      : "memory");
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8) that wait on vector memory only.
+constexpr int kVmcnt0 = 0x0F70, kVmcnt2 = 0x0F72, kVmcnt10 = 0x0F7A;
+
 // Wave-uniform integer kept in a scalar register (buffer descriptor fields
 // must be scalar; clamps otherwise tend to land in vector registers).
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -229,11 +256,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   const int npairs = G * nq;
   const int wk_lo = kv0 + 32 * kKT * w;
 
-  // Prefetch registers: PF chunks of Q and of dO per thread, plus lse / Delta.
-  u32x4 pq[C::PF], pdo[C::PF];
+  // Prefetch: Q / dO of a pair go straight into LDS (buffer_load ... lds);
+  // lse / Delta pass through registers.
   float plse = 0.0f, pdlt = 0.0f;
   int prows = 0;
-  auto load_pair = [&](int i) {
+  auto load_pair = [&](int i, int buf) {
     const int h = g * G + i / nq;
     const int q0 = (ib0 + i % nq) * BM;
     const int rows = uni(min(L - q0, BM));  // >= 1: query blocks start inside the sequence
@@ -242,10 +269,16 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     const rsrc_t dr = make_rsrc(static_cast<const T*>(p.dout) + qb, rows * q_row * 2);
 #pragma unroll
     for (int u = 0; u < C::PF; ++u) {
-      const int ci = tid + kThreads * u;
-      const uint32_t off = ((ci / C::CH) * q_row + 8 * (ci % C::CH)) * 2;
-      pq[u] = buf_load16(qr, off);
-      pdo[u] = buf_load16(dr, off);
+      // Lane l of wave w fills physical chunk P = 64 (w + kNW u) + l of the
+      // swizzled tile, i.e. row P / CH, logical chunk (P % CH) ^ swz(row).
+      // Rows past the sequence end repeat the last row: their lse is +inf,
+      // so P = dS = 0 there whatever Q / dO hold.
+      const int P = 64 * (w + kNW * u) + lane;
+      const int r = P / C::CH, ch = (P % C::CH) ^ chunk_swz<D>(r);
+      const uint32_t off = ((uint32_t)min(r, rows - 1) * q_row + 8 * ch) * 2;
+      const int lds = buf * C::QT + 1024 * (w + kNW * u);
+      lds_dma16(qr, smem + C::Q_OFF + lds, off);
+      lds_dma16(dr, smem + C::DO_OFF + lds, off);
     }
     // lse / Delta of the pair's rows; every thread issues the loads (threads
     // past the block read out of range, i.e. zero) so the number of
@@ -259,13 +292,6 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     }
   };
   auto store_pair = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < C::PF; ++u) {
-      const int ci = tid + kThreads * u;
-      const int o = rm_off<D>(ci / C::CH, 8 * (ci % C::CH));
-      *reinterpret_cast<u32x4*>(smem + C::Q_OFF + buf * C::QT + o) = pq[u];
-      *reinterpret_cast<u32x4*>(smem + C::DO_OFF + buf * C::QT + o) = pdo[u];
-    }
     if (tid < BM) {
       // rows outside the sequence (or that saw nothing) get P = 0
       const float l2 = (tid >= prows || plse == -INFINITY) ? INFINITY : plse * kLog2e;
@@ -274,9 +300,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     }
   };
 
-  load_pair(0);
+  load_pair(0, 0);
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
   store_pair(0);
-  if (npairs > 1) load_pair(1);
+  if (npairs > 1) load_pair(1, 1);
   __syncthreads();
 
   // dQ tiles of this wave (16x16x32 MFMA): query tile dq_qt, dim tiles dq_dt
@@ -414,8 +441,15 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     // -- next pair's Q / dO / lse / Delta into the other buffer; loads for
     //    the pair after it go out before this pair's atomics.
     if (i + 1 < npairs) store_pair(buf ^ 1);
-    if (i + 2 < npairs) load_pair(i + 2);
+    // The Q / dO copy of pair i + 1 must have landed: after it this wave
+    // issued the two lse / Delta loads and, except on the first pair, the
+    // 8 atomics of pair i - 1 (memory operations complete in order).
+    if (i == 0)
+      __builtin_amdgcn_s_waitcnt(kVmcnt2);
+    else
+      __builtin_amdgcn_s_waitcnt(kVmcnt10);
     __syncthreads();
+    if (i + 2 < npairs) load_pair(i + 2, buf);
 
     // -- dQ partial = dS K for this wave's two 16 x 16 tiles.  Slot (g, e)
     //    of the 16x16x32 operands holds key 32 ks + 8 g + e; k-step ks covers
@@ -433,8 +467,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
       }
       const int qcol = 16 * dq_qt + 4 * (lane & 3);
       const int dcol = 16 * dq_dt + 4 * (lane & 3);
-#pragma unroll 2
-      for (int ks = ks_lo; ks < ks_hi; ++ks) {
+      auto step = [&](int ks) {
         const int key = 32 * ks + 8 * g64 + (l16 >> 2);
         const T8 as = tr_pair<T>(dss, dst_off<BM>(key, qcol), dst_off<BM>(key + 4, qcol));
         const T8 b0 = tr_pair<T>(smem, C::K_OFF + rm_off<D>(key, dcol),
@@ -443,6 +476,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
                                  C::K_OFF + rm_off<D>(key + 4, dcol + 16));
         qacc0 = mfma16(as, b0, qacc0);
         qacc1 = mfma16(as, b1, qacc1);
+      };
+      // Full unrolling fits the register budget only at D = 64.
+      if constexpr (WIN || D == 128) {
+#pragma unroll 2
+        for (int ks = ks_lo; ks < ks_hi; ++ks) step(ks);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < kBN / 32; ++ks) step(ks);
       }
     }
     // -- region-wide fp32 atomics straight from the C layout; rows past the
