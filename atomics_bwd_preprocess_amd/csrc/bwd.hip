@@ -29,7 +29,10 @@
 //    256 keys per workgroup halve them relative to 128.
 //
 // Data movement.  K is staged once into LDS (needed as the dQ operand); V
-// (and K for D = 64) of the wave live in registers as MFMA B operands.
+// (and K for D = 64) of the wave live in registers as MFMA B operands.  At
+// D = 128 the register file is short: the last three V k-steps of each wave
+// sit in LDS instead, and lse / Delta are copied raw into LDS rather than
+// passing through registers.
 // Q / dO tiles of a pair (row-major, XOR-swizzled 16-byte chunks) and their
 // lse / Delta rows are double-buffered in LDS.  Right after pair i's barrier
 // the Q / dO tiles of pair i + 2 are copied from memory straight into the
@@ -69,9 +72,19 @@ struct Cfg {
   static constexpr int DO_OFF = Q_OFF + 2 * QT;
   static constexpr int DST = kBN * BM * 2;
   static constexpr int DS_OFF = DO_OFF + 2 * QT;
+  // lse / Delta rows of a pair: at D = 128 they are copied raw into LDS
+  // (64 floats per buffer, one wave each); otherwise they pass through
+  // registers and are stored as lse * log2(e) (+inf on rows past the end).
+  static constexpr bool LSE_DMA = D == 128;
   static constexpr int LSE_OFF = DS_OFF + 2 * DST;
-  static constexpr int DLT_OFF = LSE_OFF + 2 * BM * 4;
-  static constexpr int BYTES = DLT_OFF + 2 * BM * 4;
+  static constexpr int DLT_OFF = LSE_OFF + 2 * 64 * 4;
+  // The last VLDS k-steps of each wave's V operand live in LDS (16 bytes per
+  // lane per step, lane-linear) instead of registers: at D = 128 the
+  // register file is otherwise a dozen registers short.
+  static constexpr int VLDS = D == 128 ? 3 : 0;
+  static constexpr int VREG = D / 16 - VLDS;  // V k-steps held in registers
+  static constexpr int V_OFF = DLT_OFF + 2 * 64 * 4;
+  static constexpr int BYTES = V_OFF + VLDS * kNW * 1024;
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
   static constexpr int PF = BM * CH / kThreads;      // prefetch chunks per thread per tensor
   static constexpr int NQT = BM / 16, NDT = D / 16;  // 16x16 dQ tiles
@@ -169,7 +182,24 @@ __device__ __forceinline__ void lds_dma16(rsrc_t r, char* dst, uint32_t off) {
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8) that wait on vector memory only.
-constexpr int kVmcnt0 = 0x0F70, kVmcnt2 = 0x0F72, kVmcnt10 = 0x0F7A;
+// kVmcnt0 + n (n < 16) waits until at most n are outstanding.
+constexpr int kVmcnt0 = 0x0F70;
+
+// Same for 4 bytes per lane: lane l writes bytes [4 l, 4 l + 4) after `dst`.
+__device__ __forceinline__ void lds_dma4(rsrc_t r, char* dst, uint32_t off) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(off), "s"(r)
+      : "memory");
+}
 
 // Wave-uniform integer kept in a scalar register (buffer descriptor fields
 // must be scalar; clamps otherwise tend to land in vector registers).
@@ -225,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
         buf_load16(kr, (r * kv_row + 8 * ch) * 2);
   }
   // ---- V (and K for D = 64) of this wave's keys as MFMA B operands ---------
-  T8 vreg[kKT][D / 16];
+  T8 vreg[kKT][C::VREG];
   T8 kreg[C::KREG ? kKT : 1][C::KREG ? D / 16 : 1];
 #pragma unroll
   for (int kt = 0; kt < kKT; ++kt) {
@@ -233,7 +263,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const uint32_t off = (row * kv_row + 16 * ks + 8 * c) * 2;
-      vreg[kt][ks] = __builtin_bit_cast(T8, buf_load16(vr, off));
+      if (ks < C::VREG)
+        vreg[kt][ks] = __builtin_bit_cast(T8, buf_load16(vr, off));
+      else
+        lds_dma16(vr, smem + C::V_OFF + ((kt * C::VLDS + ks - C::VREG) * kNW + uni(w)) * 1024, off);
       if constexpr (C::KREG) kreg[kt][ks] = __builtin_bit_cast(T8, buf_load16(kr, off));
     }
   }
@@ -271,19 +304,30 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     for (int u = 0; u < C::PF; ++u) {
       // Lane l of wave w fills physical chunk P = 64 (w + kNW u) + l of the
       // swizzled tile, i.e. row P / CH, logical chunk (P % CH) ^ swz(row).
-      // Rows past the sequence end repeat the last row: their lse is +inf,
-      // so P = dS = 0 there whatever Q / dO hold.
-      const int P = 64 * (w + kNW * u) + lane;
+      // Rows past the sequence end repeat the last row; P = dS = 0 there
+      // whatever Q / dO hold (their lse is stored as +inf, or, when lse is
+      // copied raw, the edge-tile pass masks them).
+      const int P0 = uni(64 * (w + kNW * u));  // wave-uniform
+      const int P = P0 + lane;
       const int r = P / C::CH, ch = (P % C::CH) ^ chunk_swz<D>(r);
       const uint32_t off = ((uint32_t)min(r, rows - 1) * q_row + 8 * ch) * 2;
-      const int lds = buf * C::QT + 1024 * (w + kNW * u);
+      const int lds = buf * C::QT + 16 * P0;
       lds_dma16(qr, smem + C::Q_OFF + lds, off);
       lds_dma16(dr, smem + C::DO_OFF + lds, off);
     }
-    // lse / Delta of the pair's rows; every thread issues the loads (threads
-    // past the block read out of range, i.e. zero) so the number of
-    // outstanding memory operations is the same in every lane.
-    {
+    // lse / Delta of the pair's rows.
+    if constexpr (C::LSE_DMA) {
+      // Waves 0 and 1 copy 64 floats each (lanes past the rows read out of
+      // range); rows past the sequence end are masked in the edge-tile pass.
+      const size_t idx = (size_t)h * p.total + a + q0;
+      const int wu = uni(w);
+      if (wu < 2)
+        lds_dma4(make_rsrc((wu == 0 ? p.lse : p.delta) + idx, rows * 4),
+                 smem + (wu == 0 ? C::LSE_OFF : C::DLT_OFF) + buf * 256, (uint32_t)lane * 4);
+    } else {
+      // every thread issues the loads (threads past the block read out of
+      // range, i.e. zero) so the number of outstanding memory operations is
+      // the same in every lane.
       const size_t idx = (size_t)h * p.total + a + q0;
       const uint32_t off = (uint32_t)(tid & (BM - 1)) * 4 + (tid < BM ? 0u : 0x40000000u);
       plse = buf_load_f32(make_rsrc(p.lse + idx, rows * 4), off);
@@ -292,11 +336,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     }
   };
   auto store_pair = [&](int buf) {
-    if (tid < BM) {
+    if (!C::LSE_DMA && tid < BM) {
       // rows outside the sequence (or that saw nothing) get P = 0
       const float l2 = (tid >= prows || plse == -INFINITY) ? INFINITY : plse * kLog2e;
-      reinterpret_cast<float*>(smem + C::LSE_OFF)[buf * BM + tid] = l2;
-      reinterpret_cast<float*>(smem + C::DLT_OFF)[buf * BM + tid] = pdlt;
+      reinterpret_cast<float*>(smem + C::LSE_OFF)[buf * 64 + tid] = l2;
+      reinterpret_cast<float*>(smem + C::DLT_OFF)[buf * 64 + tid] = pdlt;
     }
   };
 
@@ -319,8 +363,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     const char* qs = smem + C::Q_OFF + buf * C::QT;
     const char* dos = smem + C::DO_OFF + buf * C::QT;
     char* dss = smem + C::DS_OFF + buf * C::DST;
-    const float* lse2 = reinterpret_cast<const float*>(smem + C::LSE_OFF) + buf * BM;
-    const float* dlt = reinterpret_cast<const float*>(smem + C::DLT_OFF) + buf * BM;
+    const float* lse2 = reinterpret_cast<const float*>(smem + C::LSE_OFF) + buf * 64;
+    const float* dlt = reinterpret_cast<const float*>(smem + C::DLT_OFF) + buf * 64;
 
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) {
@@ -360,7 +404,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
         for (int mt = 0; mt < MT; ++mt) {
           const int o = rm_off<D>(32 * mt + n, 16 * ks + 8 * c);
           sacc[mt] = mfma32(lds16<T>(qs, o), kb, sacc[mt]);
-          pacc[mt] = mfma32(lds16<T>(dos, o), vreg[kt][ks], pacc[mt]);
+          const T8 vb = ks < C::VREG
+                            ? vreg[kt][ks]
+                            : lds16<T>(smem, C::V_OFF + ((kt * C::VLDS + ks - C::VREG) * kNW + w) * 1024 + 16 * lane);
+          pacc[mt] = mfma32(lds16<T>(dos, o), vb, pacc[mt]);
         }
       }
 
@@ -384,7 +431,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g4 + e;
-            const float pv = fast_exp2(sacc[mt][r] * p.scale_log2 - l4[e]);
+            const float l2 = C::LSE_DMA ? l4[e] * kLog2e : l4[e];
+            const float pv = fast_exp2(sacc[mt][r] * p.scale_log2 - l2);
             sacc[mt][r] = pv;
             pacc[mt][r] = pv * (pacc[mt][r] - d4[e]);
           }
@@ -400,8 +448,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int dd = q0 + 32 * mt + 8 * (r >> 2) + 4 * c + (r & 3) - kj;
-            const bool vis = kin & (dd >= dlo) & (dd <= dhi);
+            const int q = q0 + 32 * mt + 8 * (r >> 2) + 4 * c + (r & 3);
+            const int dd = q - kj;
+            const bool vis = kin & (q < L) & (dd >= dlo) & (dd <= dhi);
             sacc[mt][r] = vis ? sacc[mt][r] : 0.0f;
             pacc[mt][r] = vis ? pacc[mt][r] : 0.0f;
           }
@@ -441,13 +490,17 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     // -- next pair's Q / dO / lse / Delta into the other buffer; loads for
     //    the pair after it go out before this pair's atomics.
     if (i + 1 < npairs) store_pair(buf ^ 1);
-    // The Q / dO copy of pair i + 1 must have landed: after it this wave
-    // issued the two lse / Delta loads and, except on the first pair, the
-    // 8 atomics of pair i - 1 (memory operations complete in order).
-    if (i == 0)
-      __builtin_amdgcn_s_waitcnt(kVmcnt2);
-    else
-      __builtin_amdgcn_s_waitcnt(kVmcnt10);
+    // The copies for pair i + 1 must have landed: after them this wave
+    // issued the two lse / Delta register loads (unless those are copies
+    // too) and, except on the first pair, the 8 atomics of pair i - 1
+    // (memory operations complete in order).
+    {
+      constexpr int after = C::LSE_DMA ? 0 : 2;
+      if (i == 0)
+        __builtin_amdgcn_s_waitcnt(kVmcnt0 + after);
+      else
+        __builtin_amdgcn_s_waitcnt(kVmcnt0 + after + 8);
+    }
     __syncthreads();
     if (i + 2 < npairs) load_pair(i + 2, buf);
 

@@ -113,8 +113,10 @@ attn_status_t attn_bwd_preprocess(const attn_shape_t* shape, const void* o, cons
 /*
  * Backward main pass.  Recomputes S = Q K^T and P = exp(S*scale - lse) per
  * tile, then dV = P^T dO, dP = dO V^T, dS = P o (dP - Delta) * scale,
- * dK = dS^T Q and dQ = dS K ([ASC] review thread, kernels k1-k5 fused;
- * spec formulas).
+ * dK = dS^T Q and dQ = dS K ([ASC] review thread, kernels k1-k5 fused).
+ *  - lse must be finite on every row of every sequence, as attn_fwd
+ *    produces it whenever each query sees at least one key (always the case
+ *    under causal and window masks); rows with lse = -inf are not supported.
  *  - dq_accum (zeroed by attn_bwd_preprocess) receives dQ / scale through
  *    fp32 atomic adds issued once per (query tile, key tile) as one
  *    coalesced region-wide sweep ([TL] regional atomic add; [TRI] atomics

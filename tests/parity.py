@@ -4,8 +4,9 @@ from __future__ import annotations
 
 import numpy as np
 
-# The benchmark spec's bound, per element, for dQ/dK/dV/dsink; also applied to O,
-# lse and Delta (all O(1)-scaled quantities computed in fp32 from 16-bit data).
+# The accuracy bound per element, |gpu - ref| <= ATOL + RTOL |ref|, for
+# dQ/dK/dV/dsink; also applied to O, lse and Delta (all O(1)-scaled
+# quantities computed in fp32 from 16-bit data).
 ATOL = 2e-2
 RTOL = 2e-2
 # A tighter aggregate check that catches small systematic errors which the

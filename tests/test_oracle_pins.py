@@ -147,7 +147,8 @@ def test_invariants(causal, window, sink):
                                       * inp["q"][a:b, h]).sum(0) for h in hs)
             np.testing.assert_allclose(lhs, rhs, atol=1e-12)
     if not sink:
-        # spec form: sum_j dV_j = sum_i dO_i (per sequence and group)
+        # rows of P sum to one without a sink, so sum_j dV_j = sum_i dO_i
+        # (per sequence and group)
         for s in range(len(cu) - 1):
             a, b = int(cu[s]), int(cu[s + 1])
             np.testing.assert_allclose(g["dv"][a:b].sum(axis=(0, 1)),
