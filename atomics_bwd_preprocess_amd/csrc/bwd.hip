@@ -38,10 +38,11 @@
 // the Q / dO tiles of pair i + 2 are copied from memory straight into the
 // buffer pair i has released (buffer loads with an LDS destination, so no
 // registers are held for them); lse / Delta pass through registers.  Both go
-// out before the atomics of pair i, so they never queue behind them.  Transposed operands (dO, Q for
-// dV / dK; dS, K for dQ) come from gfx950's transposing LDS read, and dS is
-// stored key-major with 8-byte writes.  All LDS patterns are bank-conflict
-// free under the measured bank model (see the swizzle notes below).
+// out before the atomics of pair i, so they never queue behind them.
+// Transposed operands (dO, Q for dV / dK; dS, K for dQ) come from gfx950's
+// transposing LDS read, and dS is stored key-major with 8-byte writes.  All
+// LDS patterns are bank-conflict free under the measured bank model
+// (row-major swizzle in common.h, dS swizzle below).
 // One workgroup barrier per pair.
 //
 // The sink needs no term here: it only enters through lse.
@@ -109,27 +110,6 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// LDS bank model (measured on MI355X): 64 banks of 4 bytes; 16-byte accesses
-// resolve in passes of 16 lanes, 8-byte and transposing accesses in passes of
-// 32 lanes.  The swizzles below make every access pattern of this kernel
-// conflict-free under that model (checked exhaustively by the host model of
-// the LDS layout in the tests).
-//
-// Row-major tiles (D columns): 16-byte chunk c of row r lives at chunk
-// c ^ chunk_swz(r): 16 consecutive rows hit 16 distinct chunks (16-byte operand
-// reads), and 4 consecutive rows spread a 64-byte column block over the whole
-// bank range (transposing reads).
-template <int D>
-__device__ __forceinline__ int chunk_swz(int r) {
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
-}
-template <int D>
-__device__ __forceinline__ int rm_off(int r, int col) {  // col: multiple of 4
-  return r * (D * 2) + (((col >> 3) ^ chunk_swz<D>(r)) << 4) + ((col & 7) << 1);
-}
 // Key-major dS tile (BM queries per row): 8-byte slot s of row r lives at
 // slot s ^ slot_swz(r).
 template <int BM>
@@ -141,73 +121,6 @@ __device__ __forceinline__ int slot_swz(int r) {
 template <int BM>
 __device__ __forceinline__ int dst_off(int r, int q) {  // q: multiple of 4
   return r * (BM * 2) + (((q >> 2) ^ slot_swz<BM>(r)) << 3);
-}
-
-// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
-// i receives element (i % 4) of the 8-byte pieces addressed by lanes
-// 4e + i / 4, e = 0..3.  Lanes address row k0 + p / 4, columns n0 + 4 (p % 4)
-// (p = lane % 16) of a row-major matrix; lane i then holds rows k0..k0+3 of
-// column n0 + i.
-__device__ __forceinline__ u32x2 tr_read(const char* smem, int off) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + off));
-  return __builtin_bit_cast(u32x2, v);
-}
-template <typename T>
-__device__ __forceinline__ typename V8<T>::type tr_pair(const char* smem, int off_lo, int off_hi) {
-  const u32x2 lo = tr_read(smem, off_lo), hi = tr_read(smem, off_hi);
-  const u32x4 r = {lo[0], lo[1], hi[0], hi[1]};
-  return __builtin_bit_cast(typename V8<T>::type, r);
-}
-
-// 16 bytes per lane from a buffer straight into LDS: lane l writes bytes
-// [16 l, 16 l + 16) after the wave-uniform LDS address `dst`.  Issued as
-// inline assembly so the compiler's wait-count bookkeeping does not follow
-// it (it would otherwise wait for the load before the next LDS access);
-// the kernel waits for it explicitly before the barrier that publishes it.
-// M0 (which supplies the LDS address) is saved and restored around it.
-__device__ __forceinline__ void lds_dma16(rsrc_t r, char* dst, uint32_t off) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(base), "v"(off), "s"(r)
-      : "memory");
-}
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8) that wait on vector memory only.
-// kVmcnt0 + n (n < 16) waits until at most n are outstanding.
-constexpr int kVmcnt0 = 0x0F70;
-
-// Same for 4 bytes per lane: lane l writes bytes [4 l, 4 l + 4) after `dst`.
-__device__ __forceinline__ void lds_dma4(rsrc_t r, char* dst, uint32_t off) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(base), "v"(off), "s"(r)
-      : "memory");
-}
-
-// Wave-uniform integer kept in a scalar register (buffer descriptor fields
-// must be scalar; clamps otherwise tend to land in vector registers).
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-template <typename T>
-__device__ __forceinline__ typename V8<T>::type lds16(const char* smem, int off) {
-  return __builtin_bit_cast(typename V8<T>::type, *reinterpret_cast<const u32x4*>(smem + off));
 }
 
 // WIN: sliding-window problems, where most key tiles of a query block are

@@ -3,14 +3,22 @@
 // forward kernel of its 2-kernel architecture, producing O and lse).
 //
 // gfx950 design: one workgroup = 4 waves = 128 query rows of one (sequence,
-// query head); wave w owns rows [32w, 32w + 32).  Its Q rows stay in
-// registers as the MFMA B operand.  The loop walks 64-key blocks staged in LDS
-// (K row-major, V transposed) and computes, per wave,
-//     S^T = K Q^T      (32x32x16 MFMA, K from LDS, Q^T from registers)
-//     O^T += V^T P^T   (P^T is consumed directly from the MFMA C layout)
+// query head), two workgroups per CU; wave w owns rows [32w, 32w + 32) and
+// keeps its Q rows in registers as the MFMA B operand.  The loop walks
+// 64-key blocks.  Each block's K and V tiles are copied from memory straight
+// into LDS (buffer loads with an LDS destination; row-major tiles with
+// XOR-swizzled 16-byte chunks, double-buffered, issued one block ahead), and
+// per wave
+//     S^T = K Q^T      (32x32x16 MFMA, K rows from LDS, Q^T from registers)
+//     O^T += V^T P^T   (V^T from the transposing LDS read, P^T straight from
+//                       the MFMA C layout of S^T)
 // so the softmax statistics of one query live in one lane pair (l, l ^ 32).
-// The sink initialises the running max and sum (m = sink, l = 1), which adds
-// exp(sink) to the denominator without a value vector.
+// The running maximum is taken over raw scores (the scale is positive) and
+// the scale folds into the exponent's FMA.  The sink initialises the running
+// max and sum (m = sink, l = 1), which adds exp(sink) to the denominator
+// without a value vector.  A wave skips the blocks that are masked for all
+// of its rows, masks are applied only on blocks that need them, and there is
+// one workgroup barrier per block.
 #include "common.h"
 #include "launch.h"
 
@@ -20,6 +28,19 @@ namespace {
 
 constexpr int kFwdBM = 128;  // query rows per workgroup
 constexpr int kFwdBN = 64;   // keys per block
+constexpr int kFwdNW = 4;    // waves per workgroup
+constexpr int kFwdThreads = 64 * kFwdNW;
+
+template <int D>
+struct FwdCfg {
+  static constexpr int CH = D / 8;                               // 16-byte chunks per row
+  static constexpr int TILE = kFwdBN * D * 2;                    // bytes of a K or V tile
+  static constexpr int STAGE = 2 * TILE;                         // K tile, then V tile
+  static constexpr int BYTES = 2 * STAGE;                        // two stages
+  static constexpr int NDMA = 2 * kFwdBN * CH / kFwdThreads;     // 16-byte copies per thread per block
+  static_assert(kFwdBN * CH % 64 == 0 && NDMA * kFwdThreads == 2 * kFwdBN * CH, "copy split");
+  static_assert(2 * BYTES <= 160 * 1024, "two workgroups per CU");
+};
 
 struct FwdArgs {
   const void* q;
@@ -35,19 +56,15 @@ struct FwdArgs {
 };
 
 template <typename T, int D>
-struct FwdSmem {
-  alignas(16) T k[kFwdBN][D + 8];
-  alignas(16) T vt[D][kFwdBN + 8];
-};
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
+__global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
+  using C = FwdCfg<D>;
   using T8 = typename V8<T>::type;
   using T4 = typename V8<T>::half_type;
-  __shared__ FwdSmem<T, D> sm;
+  __shared__ __attribute__((aligned(16))) char smem[C::BYTES];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, n = lane & 31, c = lane >> 5;
+  const int l16 = lane & 15, g16 = (lane >> 4) & 1;
 
   // Longest work first: the largest query-block index of every (seq, head)
   // is dispatched before smaller ones.
@@ -61,20 +78,21 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
   const int q0 = qb * kFwdBM;
   if (q0 >= L) return;
   const int g = h / (p.hq / p.hkv);
-  const T* __restrict__ qp = static_cast<const T*>(p.q);
-  const T* __restrict__ kp = static_cast<const T*>(p.k);
-  const T* __restrict__ vp = static_cast<const T*>(p.v);
+  const uint32_t kv_row = (uint32_t)p.hkv * D;  // elements between key rows
+  const uint32_t q_row = (uint32_t)p.hq * D;    // elements between query rows
 
-  // This lane's query (B-operand column n of wave w).
+  // This lane's query (B-operand column n of wave w); rows past the sequence
+  // end read as zero.
   const int qi = q0 + 32 * w + n;
-  const bool qvalid = qi < L;
+  const int qrows = uni(min(L - q0, kFwdBM));
+  const rsrc_t qr = make_rsrc(static_cast<const T*>(p.q) + ((size_t)(a + q0) * p.hq + h) * D,
+                              qrows * q_row * 2);
   T8 qreg[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks)
-    qreg[ks] = qvalid ? ld16<T>(qp + ((size_t)(a + qi) * p.hq + h) * D + 16 * ks + 8 * c)
-                      : zero8<T>();
+    qreg[ks] = __builtin_bit_cast(T8, buf_load16(qr, ((32 * w + n) * q_row + 16 * ks + 8 * c) * 2));
 
-  float m_run, l_run;
+  float m_run, l_run;  // running max (scaled, log2 units) and sum
   if (p.sink) {
     m_run = p.sink[h] * kLog2e;
     l_run = 1.0f;
@@ -92,100 +110,117 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
   if (p.causal) k_hi = qlast + 1;
   if (p.window > 0) k_lo = max(0, q0 - p.window + 1);
   k_lo = (k_lo / kFwdBN) * kFwdBN;
-  // Rows of this wave (for the mask decision).
+  // Rows of this wave (for the skip and mask decisions).
   const int wq_lo = q0 + 32 * w, wq_hi = min(q0 + 32 * w + 31, L - 1);
 
-  for (int kb = k_lo; kb < k_hi; kb += kFwdBN) {
-    __syncthreads();
-    // K block, row-major: 64 rows x D / 8 chunks of 16 bytes.
-    for (int u = tid; u < kFwdBN * (D / 8); u += 256) {
-      const int r = u / (D / 8), dc = u % (D / 8);
-      const int j = kb + r;
-      st16<T>(&sm.k[r][8 * dc],
-              j < L ? ld16<T>(kp + ((size_t)(a + j) * p.hkv + g) * D + 8 * dc) : zero8<T>());
+  // Copy keys [kb, kb + 64) of K and V into stage `stage`.  Lane l of wave w
+  // fills physical chunk 64 (w + 4 u) + l of the K tile followed by the V
+  // tile: row P / CH, logical chunk (P % CH) ^ swz(row).  Rows past the
+  // sequence end repeat its last key (finite values; masked below).
+  const T* kp = static_cast<const T*>(p.k);
+  const T* vp = static_cast<const T*>(p.v);
+  auto issue = [&](int kb, int stage) {
+    const int nk = uni(min(L - kb, kFwdBN));
+    const size_t base = ((size_t)(a + kb) * p.hkv + g) * D;
+    const rsrc_t kr = make_rsrc(kp + base, nk * kv_row * 2);
+    const rsrc_t vr = make_rsrc(vp + base, nk * kv_row * 2);
+#pragma unroll
+    for (int u = 0; u < C::NDMA; ++u) {
+      const int P0 = uni(64 * (w + kFwdNW * u));
+      const bool isv = P0 >= kFwdBN * C::CH;
+      const int Pt = P0 - (isv ? kFwdBN * C::CH : 0);  // first chunk of the wave in its tile
+      const int P = Pt + lane;
+      const int r = P / C::CH, ch = (P % C::CH) ^ chunk_swz<D>(r);
+      const uint32_t off = ((uint32_t)min(r, nk - 1) * kv_row + 8 * ch) * 2;
+      lds_dma16(isv ? vr : kr, smem + stage * C::STAGE + (isv ? C::TILE : 0) + 16 * Pt, off);
     }
-    // V block, transposed through registers: a unit is 4 keys x 8 dims.
-    for (int u = tid; u < (kFwdBN / 4) * (D / 8); u += 256) {
-      const int rg = u / (D / 8), dc = u % (D / 8);
-      T8 rows[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = kb + 4 * rg + e;
-        rows[e] = j < L ? ld16<T>(vp + ((size_t)(a + j) * p.hkv + g) * D + 8 * dc) : zero8<T>();
-      }
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        T4 col;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) col[e] = rows[e][dd];
-        st8<T>(&sm.vt[8 * dc + dd][4 * rg], col);
-      }
-    }
-    __syncthreads();
-    if (wq_lo > wq_hi) continue;  // wave entirely past the sequence end
+  };
 
-    // S^T for keys [kb, kb + 64) (two 32-row tiles) against this wave's queries.
-    f32x16 st[2] = {f32x16{}, f32x16{}};
+  issue(k_lo, 0);
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  __syncthreads();
+  int stage = 0;
+  for (int kb = k_lo; kb < k_hi; kb += kFwdBN, stage ^= 1) {
+    // The other stage was last read before the previous barrier.
+    if (kb + kFwdBN < k_hi) issue(kb + kFwdBN, stage ^ 1);
+
+    const bool skip = wq_lo > wq_hi || (p.causal && kb > wq_hi) ||
+                      (p.window > 0 && kb + kFwdBN - 1 <= wq_lo - p.window);
+    if (!skip) {
+      const char* kt = smem + stage * C::STAGE;
+      const char* vt = kt + C::TILE;
+
+      // S^T for keys [kb, kb + 64) (two 32-row tiles) against this wave's queries.
+      f32x16 st[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+      for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          st[mt] = mfma32(lds16<T>(kt, rm_off<D>(32 * mt + n, 16 * ks + 8 * c)), qreg[ks], st[mt]);
+
+      // Hidden keys -> -inf, only on blocks not fully visible to every row of
+      // the wave.  The empty asm keeps this a real branch.
+      const int kb_last = kb + kFwdBN - 1;
+      const bool full = (kb_last < L) && (!p.causal || kb_last <= wq_lo) &&
+                        (p.window <= 0 || kb > wq_hi - p.window);
+      if (!full) {
+        asm volatile("");
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = kb + 32 * mt + (r >> 2) * 8 + 4 * c + (r & 3);
+            if (j >= L || !visible(qi, j, p.causal, p.window)) st[mt][r] = -INFINITY;
+          }
+      }
+
+      // Online softmax over raw scores: the maximum is scaled afterwards.
+      float mraw = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        st[mt] = mfma32(ld16<T>(&sm.k[32 * mt + n][16 * ks + 8 * c]), qreg[ks], st[mt]);
-    }
-
-    // Mask only blocks that are not fully visible to every row of this wave.
-    const int kb_last = kb + kFwdBN - 1;
-    const bool full = (kb_last < L) && (!p.causal || kb_last <= wq_lo) &&
-                      (p.window <= 0 || kb > wq_hi - p.window);
-    float mloc = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+        for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, st[mt][r]);
+      mraw = fmaxf(mraw, xor32(mraw));
+      const float m_new = fmaxf(m_run, mraw * p.scale_log2);
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float lsum = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = st[mt][r] * p.scale_log2;
-        if (!full) {
-          const int j = kb + 32 * mt + (r >> 2) * 8 + 4 * c + (r & 3);
-          if (j >= L || !visible(qi, j, p.causal, p.window)) x = -INFINITY;
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = fast_exp2(st[mt][r] * p.scale_log2 - m_use);
+          st[mt][r] = pv;
+          lsum += pv;
         }
-        st[mt][r] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    }
-    mloc = fmaxf(mloc, xor32(mloc));
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float lsum = 0.0f;
+      lsum += xor32(lsum);
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(st[mt][r] - m_use);
-        st[mt][r] = pv;
-        lsum += pv;
-      }
-    }
-    lsum += xor32(lsum);
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
+      for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
 
-    // O^T += V^T P^T over the 64 keys in four 16-key steps.  Slot (c, e) of
-    // step ks holds key 16 ks + (e / 4) * 8 + 4 c + e % 4, which is where the
-    // C layout of S^T already keeps it.
+      // O^T += V^T P^T over the 64 keys in four 16-key steps.  Slot (c, e)
+      // of step ks holds key 16 ks + (e / 4) * 8 + 4 c + e % 4, which is
+      // where the C layout of S^T already keeps it; the transposing read of
+      // the row-major V tile delivers the A operand in the same order.
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const T8 pb = pack8<T>(st[ks >> 1], 8 * (ks & 1));
+      for (int ks = 0; ks < kFwdBN / 16; ++ks) {
+        const T8 pb = pack8<T>(st[ks >> 1], 8 * (ks & 1));
+        const int row = 16 * ks + 4 * c + (l16 >> 2);
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        const T* row = &sm.vt[32 * t + n][16 * ks + 4 * c];
-        oacc[t] = mfma32(cat8<T>(ld8<T>(row), ld8<T>(row + 8)), pb, oacc[t]);
+        for (int t = 0; t < D / 32; ++t) {
+          const int col = 32 * t + 16 * g16 + 4 * (lane & 3);
+          oacc[t] = mfma32(tr_pair<T>(vt, rm_off<D>(row, col), rm_off<D>(row + 8, col)), pb, oacc[t]);
+        }
       }
     }
+    // The next block's copies have landed and every wave is done with this
+    // stage before it is overwritten.
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
   }
 
-  if (!qvalid) return;
+  if (qi >= L) return;
   const bool any = l_run > 0.0f;
   const float inv = any ? 1.0f / l_run : 0.0f;
   T* __restrict__ op = static_cast<T*>(p.o) + ((size_t)(a + qi) * p.hq + h) * D;
@@ -206,7 +241,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs p) {
 template <typename T, int D>
 hipError_t fwd_t(const FwdArgs& args, hipStream_t stream) {
   const unsigned blocks = (unsigned)args.nqb * args.num_seqs * args.hq;
-  hipLaunchKernelGGL((fwd_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, args);
+  hipLaunchKernelGGL((fwd_kernel<T, D>), dim3(blocks), dim3(kFwdThreads), 0, stream, args);
   return hipGetLastError();
 }
 

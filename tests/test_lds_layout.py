@@ -10,8 +10,9 @@ patterns and the SQ_LDS_BANK_CONFLICT counter, which it reproduces exactly):
 64 banks of 4 bytes; 16-byte accesses are resolved in passes of 16 lanes,
 8-byte accesses and transposing reads (ds_read_b64_tr_b16) in passes of 32
 lanes; a pass costs one extra cycle per additional distinct dword mapped to
-its busiest bank.  The formulas below mirror chunk_swz / slot_swz in
-csrc/bwd.hip.
+its busiest bank.  The formulas below mirror chunk_swz (csrc/common.h) and
+slot_swz (csrc/bwd.hip).  The forward kernel uses the same row-major tiles
+for its 64-key K and V blocks.
 """
 import itertools
 from collections import defaultdict
@@ -145,3 +146,16 @@ def test_transposed_ds_writes_and_reads(d, bm):
     for ks, qt, half in itertools.product(range(8), range(bm // 16), (0, 4)):
         a = [dst_byte(*tr16(l, 32 * ks + half, 16 * qt), bm) for l in range(64)]
         assert instr_conflicts(a, 8) == 0, (ks, qt, half)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_forward_tiles(d):
+    # K rows as the A operand of S^T: lane l reads key 32 mt + l % 32, chunk 2 ks + l / 32
+    for mt, ks in itertools.product(range(2), range(d // 16)):
+        a = [rm_byte(32 * mt + l % 32, 8 * (2 * ks + l // 32), d) for l in range(64)]
+        assert instr_conflicts(a, 16) == 0, (mt, ks)
+    # V^T as the A operand of O^T: transposing reads of keys 16 ks + 4 c + p/4
+    # (and + 8), dims of tile t
+    for ks, t, half in itertools.product(range(4), range(d // 32), (0, 8)):
+        a = [rm_byte(*tr32(l, 16 * ks + half, 32 * t, 4), d) for l in range(64)]
+        assert instr_conflicts(a, 8) == 0, (ks, t, half)
