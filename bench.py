@@ -265,7 +265,9 @@ def main(argv=None) -> int:
                                                    * 1e-3) / 1e12, 2),
                           "attn_bwd_kernel_tflops": round(f / (rr["bwd_ms"] * 1e-3) / 1e12, 2),
                           "attn_bwd_ms": round(rr["bwd_ms"], 4),
-                          "frac": round(f / (rr["bwd_ms"] * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
+                          "frac": round(f / (rr["bwd_ms"] * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                          "fwd_tflops": round(fwd_flops(xx) / (rr["fwd_ms"] * 1e-3) / 1e12, 2),
+                          "attn_fwd_ms": round(rr["fwd_ms"], 4)}
             print(f"bench: {key}: {extra[key]}", file=sys.stderr, flush=True)
         line["per_workload"] = extra
     if not args.no_cpu_baseline:
