@@ -119,6 +119,15 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
   // sequence end repeat its last key (finite values; masked below).
   const T* kp = static_cast<const T*>(p.k);
   const T* vp = static_cast<const T*>(p.v);
+  // Per-lane source offsets within a full block (loop-invariant).
+  uint32_t coff[C::NDMA];
+#pragma unroll
+  for (int u = 0; u < C::NDMA; ++u) {
+    const int Pt = (64 * (w + kFwdNW * u)) % (kFwdBN * C::CH);
+    const int P = Pt + lane;
+    const int r = P / C::CH, ch = (P % C::CH) ^ chunk_swz<D>(r);
+    coff[u] = ((uint32_t)r * kv_row + 8 * ch) * 2;
+  }
   auto issue = [&](int kb, int stage) {
     const int nk = uni(min(L - kb, kFwdBN));
     const size_t base = ((size_t)(a + kb) * p.hkv + g) * D;
@@ -129,9 +138,12 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
       const int P0 = uni(64 * (w + kFwdNW * u));
       const bool isv = P0 >= kFwdBN * C::CH;
       const int Pt = P0 - (isv ? kFwdBN * C::CH : 0);  // first chunk of the wave in its tile
-      const int P = Pt + lane;
-      const int r = P / C::CH, ch = (P % C::CH) ^ chunk_swz<D>(r);
-      const uint32_t off = ((uint32_t)min(r, nk - 1) * kv_row + 8 * ch) * 2;
+      uint32_t off = coff[u];
+      if (nk < kFwdBN) {  // tail block: rows past the end repeat the last key
+        const int P = Pt + lane;
+        const int r = P / C::CH, ch = (P % C::CH) ^ chunk_swz<D>(r);
+        off = ((uint32_t)min(r, nk - 1) * kv_row + 8 * ch) * 2;
+      }
       lds_dma16(isv ? vr : kr, smem + stage * C::STAGE + (isv ? C::TILE : 0) + 16 * Pt, off);
     }
   };
@@ -195,9 +207,13 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
         }
       lsum += xor32(lsum);
       l_run = l_run * alpha + lsum;
-      m_run = m_new;
+      // alpha is exactly 1 on lanes whose maximum did not move; skip the
+      // rescale when that holds for the whole wave.
+      if (!__all(m_new == m_run)) {
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
+        for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
+      }
+      m_run = m_new;
 
       // O^T += V^T P^T over the 64 keys in four 16-key steps.  Slot (c, e)
       // of step ks holds key 16 ks + (e / 4) * 8 + 4 c + e % 4, which is
