@@ -32,6 +32,10 @@ import attn_inputs as ai  # noqa: E402
 METRIC = "attn_bwd TFLOP/s (fp16/bf16, causal GQA) + MFMA util vs MI355X peak"
 PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+# Device-wide rate of device-scope fp32 atomic adds, measured on MI355X with a
+# microbenchmark (1.1-1.25 TB/s whatever the workgroup count, bytes per wave
+# instruction, return / no return and working-set size).
+ATOMIC_CEILING_GBS = 1250.0
 # Pages' number for this exact workload (triton issue "atomic_add slows down
 # attention backwards": fp16, batch 4, 8 heads, d64, causal, N = 32768,
 # atomic_add after vectorized atomics; other hardware -- context only).
@@ -51,6 +55,29 @@ def bwd_flops(x: dict) -> float:
     else:
         pairs = float((lengths ** 2).sum())
     return 10.0 * hq * d * pairs
+
+
+def bwd_atomic_bytes(x: dict) -> float:
+    """Bytes of fp32 dQ atomics the main kernel issues per launch: one
+    BM x D sweep per (key block of 256, query head, query block the masks let
+    see the key block), with BM = 32 at D = 128 and 64 at D = 64 -- the
+    kernel's own schedule (rows past a sequence end are dropped by the
+    hardware and not counted)."""
+    bn, d, w = 256, x["d"], x["window"]
+    bm = 32 if d == 128 else 64
+    g = x["hq"] // x["hkv"]
+    pairs = 0
+    for L in x["lengths"]:
+        for kv0 in range(0, L, bn):
+            kv_last = min(L, kv0 + bn) - 1
+            ib0 = kv0 // bm if x["causal"] else 0
+            ib1 = (L + bm - 1) // bm
+            if w > 0:
+                ib1 = min(ib1, (kv_last + w - 1) // bm + 1)
+            # rows actually inside the sequence
+            for ib in range(ib0, ib1):
+                pairs += min(bm, L - ib * bm)
+    return float(pairs) * g * x["hkv"] * d * 4.0
 
 
 def fwd_flops(x: dict) -> float:
@@ -243,6 +270,12 @@ def main(argv=None) -> int:
                     "attn_bwd_postprocess": round(post_b / (r["post_ms"] * 1e-3) / 1e9, 1),
                     "peak": PEAK_HBM_GBS},
         "fwd_tflops": round(fwd_flops(x) / (r["fwd_ms"] * 1e-3) / 1e12, 3),
+        "atomics": {"kernel": "attn_bwd main kernel",
+                    "bytes_per_launch": bwd_atomic_bytes(x),
+                    "achieved_gbs": round(bwd_atomic_bytes(x) / (r["bwd_ms"] * 1e-3) / 1e9, 1),
+                    "ceiling_gbs": ATOMIC_CEILING_GBS,
+                    "note": "device-scope fp32 atomic adds resolve beyond L2 on this part; "
+                            "their device-wide rate, not the MFMA peak, bounds this kernel"},
         "wall_ms_per_step": round(r["wall_ms_per_step"], 4),
     }
     base = PAGES_BASELINE.get((w.name, args.n if w.name == "mha_causal" else None))
@@ -266,6 +299,7 @@ def main(argv=None) -> int:
                           "attn_bwd_kernel_tflops": round(f / (rr["bwd_ms"] * 1e-3) / 1e12, 2),
                           "attn_bwd_ms": round(rr["bwd_ms"], 4),
                           "frac": round(f / (rr["bwd_ms"] * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                          "atomic_gbs": round(bwd_atomic_bytes(xx) / (rr["bwd_ms"] * 1e-3) / 1e9, 1),
                           "fwd_tflops": round(fwd_flops(xx) / (rr["fwd_ms"] * 1e-3) / 1e12, 2),
                           "attn_fwd_ms": round(rr["fwd_ms"], 4)}
             print(f"bench: {key}: {extra[key]}", file=sys.stderr, flush=True)
