@@ -2,6 +2,9 @@
 
 Every ``csrc/*.hip`` file is compiled to an object under ``_build/`` (in
 parallel) and linked into ``atomics_bwd_preprocess_amd/libattn_bwd.so``.
+``microbench/atomic_rate.hip`` (the atomic-rate measurement the benchmark
+script runs; not part of the attention ABI) is linked into
+``libattn_microbench.so`` beside it.
 Run ``python -m atomics_bwd_preprocess_amd.build`` or call ``build()``.
 """
 from __future__ import annotations
@@ -17,6 +20,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libattn_bwd.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+MICROBENCH_SRC = os.path.join(PKG_DIR, "microbench", "atomic_rate.hip")
+MICROBENCH_LIB = os.path.join(PKG_DIR, "libattn_microbench.so")
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for every device compile.
@@ -57,24 +62,30 @@ def sources() -> list:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build(verbose: bool = False, extra_flags: list | None = None) -> str:
-    """Compile and link the library; returns its path.  Always rebuilds."""
-    hipcc = _hipcc()
-    extra = list(extra_flags or [])
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
-    workers = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(workers) as ex:
-        list(ex.map(lambda so: _compile(hipcc, so[0], so[1], extra), zip(srcs, objs)))
-    tmp = LIB_PATH + ".tmp"
+def _link(hipcc: str, objs: list, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, extra_flags: list | None = None) -> str:
+    """Compile and link the library (and the microbenchmark library); returns
+    the library's path.  Always rebuilds."""
+    hipcc = _hipcc()
+    extra = list(extra_flags or [])
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources() + [MICROBENCH_SRC]
+    objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    workers = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda so: _compile(hipcc, so[0], so[1], extra), zip(srcs, objs)))
+    _link(hipcc, objs[:-1], LIB_PATH)
+    _link(hipcc, objs[-1:], MICROBENCH_LIB)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {MICROBENCH_LIB}")
     return LIB_PATH
 
 

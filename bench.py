@@ -34,8 +34,11 @@ PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 # Device-wide rate of device-scope fp32 atomic adds, measured on MI355X with a
 # microbenchmark (1.1-1.25 TB/s whatever the workgroup count, bytes per wave
-# instruction, return / no return and working-set size).
+# instruction, return / no return and working-set size).  bench.py measures
+# it again on the machine it runs on (microbench/atomic_rate.hip); this figure
+# is used only if that library is missing.
 ATOMIC_CEILING_GBS = 1250.0
+MICROBENCH_LIB = os.path.join(ROOT, "atomics_bwd_preprocess_amd", "libattn_microbench.so")
 # Pages' number for this exact workload (triton issue "atomic_add slows down
 # attention backwards": fp16, batch 4, 8 heads, d64, causal, N = 32768,
 # atomic_add after vectorized atomics; other hardware -- context only).
@@ -78,6 +81,36 @@ def bwd_atomic_bytes(x: dict) -> float:
             for ib in range(ib0, ib1):
                 pairs += min(bm, L - ib * bm)
     return float(pairs) * g * x["hkv"] * d * 4.0
+
+
+def atomic_ceiling_gbs():
+    """Live device-wide rate of device-scope fp32 atomic adds (GB/s of added
+    data): 32768 waves each adding to a 256-byte segment per iteration over a
+    256 MiB buffer, timed with HIP events over three launches."""
+    import ctypes
+
+    import torch
+
+    if not os.path.exists(MICROBENCH_LIB):
+        return None
+    lib = ctypes.CDLL(MICROBENCH_LIB)
+    f = lib.attn_microbench_atomic_rate
+    f.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    nseg, blocks, iters, reps = 1 << 20, 8192, 64, 3
+    buf = torch.zeros(nseg * 64, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    if f(buf.data_ptr(), nseg, blocks, iters, stream.cuda_stream) != 0:
+        return None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        f(buf.data_ptr(), nseg, blocks, iters, stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    del buf
+    return reps * blocks * 256 * iters * 4 / (ms * 1e-3) / 1e9
 
 
 def fwd_flops(x: dict) -> float:
@@ -242,6 +275,7 @@ def main(argv=None) -> int:
     value = fl / (bwd_total_ms * 1e-3) / 1e12
     kernel_tflops = fl / (r["bwd_ms"] * 1e-3) / 1e12
     traffic = _traffic(w.name if w.name != "mha_causal" else f"mha_causal_n{args.n}")
+    ceiling = atomic_ceiling_gbs()
     pre_b, post_b = prepost_bytes(x)
     line = {
         "metric": METRIC,
@@ -273,7 +307,9 @@ def main(argv=None) -> int:
         "atomics": {"kernel": "attn_bwd main kernel",
                     "bytes_per_launch": bwd_atomic_bytes(x),
                     "achieved_gbs": round(bwd_atomic_bytes(x) / (r["bwd_ms"] * 1e-3) / 1e9, 1),
-                    "ceiling_gbs": ATOMIC_CEILING_GBS,
+                    "ceiling_gbs": round(ceiling, 1) if ceiling else ATOMIC_CEILING_GBS,
+                    "ceiling_source": ("measured in this run (microbench/atomic_rate.hip)"
+                                       if ceiling else "earlier microbenchmark figure"),
                     "note": "device-scope fp32 atomic adds resolve beyond L2 on this part; "
                             "their device-wide rate, not the MFMA peak, bounds this kernel"},
         "wall_ms_per_step": round(r["wall_ms_per_step"], 4),
