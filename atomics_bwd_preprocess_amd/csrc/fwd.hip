@@ -67,17 +67,22 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
   const int l16 = lane & 15, g16 = (lane >> 4) & 1;
 
   // Longest work first: the largest query-block index of every (seq, head)
-  // is dispatched before smaller ones.
+  // is dispatched before smaller ones.  Within one query-block index the kv
+  // group varies fastest, so (with Hkv a multiple of 8) every head of a group
+  // lands on the same XCD -- workgroups are dealt round-robin over the 8
+  // XCDs -- and the group's K / V blocks are shared through one L2.
   const int nsh = p.num_seqs * p.hq;
+  const int G = p.hq / p.hkv;
   const int qb = p.nqb - 1 - (int)(blockIdx.x / nsh);
   const int rem = blockIdx.x % nsh;
-  const int s = rem / p.hq, h = rem % p.hq;
+  const int s = rem / p.hq;
+  const int h = (rem % p.hkv) * G + (rem % p.hq) / p.hkv;
   int a, b;
   seq_bounds(p.cu, s, p.max_seqlen, p.total, a, b);
   const int L = b - a;
   const int q0 = qb * kFwdBM;
   if (q0 >= L) return;
-  const int g = h / (p.hq / p.hkv);
+  const int g = h / G;
   const uint32_t kv_row = (uint32_t)p.hkv * D;  // elements between key rows
   const uint32_t q_row = (uint32_t)p.hq * D;    // elements between query rows
 
