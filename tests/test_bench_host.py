@@ -1,0 +1,67 @@
+"""Host logic of bench.py (no GPU): the FLOP convention, the dQ atomic byte
+count (which must follow the main kernel's schedule) and the one-GPU rule."""
+import itertools
+
+import pytest
+
+import bench
+from test_tile_schedule import q_range
+
+
+def _x(lengths, hq=4, hkv=2, d=64, causal=True, window=0):
+    return dict(lengths=list(lengths), hq=hq, hkv=hkv, d=d, causal=causal, window=window,
+                sink=None)
+
+
+def _visible_pairs(lengths, causal, window):
+    n = 0
+    for L in lengths:
+        for i, j in itertools.product(range(L), range(L)):
+            n += (not causal or j <= i) and (window <= 0 or j > i - window)
+    return n
+
+
+@pytest.mark.parametrize("lengths", [[1], [7, 33], [64, 5, 100]])
+def test_flop_convention(lengths):
+    hq, d = 4, 64
+    # full attention: every pair; causal: the usual N^2 / 2 convention
+    assert bench.bwd_flops(_x(lengths, causal=False)) == 10 * hq * d * sum(L * L for L in lengths)
+    assert bench.bwd_flops(_x(lengths)) == 10 * hq * d * sum(L * L for L in lengths) / 2
+    # a window counts exactly the visible pairs
+    for w in (1, 3, 17):
+        assert bench.bwd_flops(_x(lengths, window=w)) == \
+            10 * hq * d * _visible_pairs(lengths, True, w)
+    assert bench.fwd_flops(_x(lengths)) == pytest.approx(0.4 * bench.bwd_flops(_x(lengths)))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,w", [(False, 0), (True, 0), (True, 1), (True, 37), (True, 300)])
+def test_atomic_bytes_follow_the_schedule(d, causal, w):
+    bm = 32 if d == 128 else 64
+    lengths = [1, 31, 257, 700]
+    hq, hkv = 8, 2
+    rows = 0
+    for L in lengths:
+        for kv0 in range(0, L, 256):
+            ib0, ib1 = q_range(L, kv0, bm, causal, w)
+            rows += sum(min(bm, L - ib * bm) for ib in range(ib0, ib1))
+            # every query row that sees a key of the block is swept
+            keys = range(kv0, min(L, kv0 + 256))
+            seen = {i for i in range(L) for j in keys
+                    if (not causal or j <= i) and (w <= 0 or j > i - w)}
+            assert all(ib0 * bm <= i < ib1 * bm for i in seen)
+    x = _x(lengths, hq=hq, hkv=hkv, d=d, causal=causal, window=w)
+    assert bench.bwd_atomic_bytes(x) == rows * hq * d * 4
+
+
+def test_headline_atomic_bytes():
+    # 4 x 32768 tokens, 8 heads, D = 64, causal: one 64 x 64 fp32 sweep per
+    # (head, key block of 256, query block at or after the block's start)
+    x = _x([32768] * 4, hq=8, hkv=8, d=64)
+    per_seq_head = sum(32768 - 256 * kb for kb in range(128))
+    assert bench.bwd_atomic_bytes(x) == 4 * 8 * per_seq_head * 64 * 4
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
