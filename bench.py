@@ -113,6 +113,28 @@ def atomic_ceiling_gbs():
     return reps * blocks * 256 * iters * 4 / (ms * 1e-3) / 1e9
 
 
+def copy_reference_gbs(mib: int = 1024) -> float:
+    """Bytes moved (read + write) per second by a plain device-to-device copy
+    of `mib` MiB through PyTorch: the practical ceiling for a kernel that
+    reads and writes about as much as it reads."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    del src, dst
+    return 2.0 * n * 4 / (ms * 1e-3) / 1e9
+
+
 def fwd_flops(x: dict) -> float:
     return bwd_flops(x) * 4.0 / 10.0
 
@@ -302,7 +324,8 @@ def main(argv=None) -> int:
                        "attn_bwd_postprocess": round(r["post_ms"], 4)},
         "hbm_gbs": {"attn_bwd_preprocess": round(pre_b / (r["pre_ms"] * 1e-3) / 1e9, 1),
                     "attn_bwd_postprocess": round(post_b / (r["post_ms"] * 1e-3) / 1e9, 1),
-                    "peak": PEAK_HBM_GBS},
+                    "peak": PEAK_HBM_GBS,
+                    "copy_reference": round(copy_reference_gbs(), 1)},
         "fwd_tflops": round(fwd_flops(x) / (r["fwd_ms"] * 1e-3) / 1e12, 3),
         "atomics": {"kernel": "attn_bwd main kernel",
                     "bytes_per_launch": bwd_atomic_bytes(x),
