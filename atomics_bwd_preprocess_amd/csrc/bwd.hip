@@ -37,8 +37,9 @@
 // lse / Delta rows are double-buffered in LDS.  Right after pair i's barrier
 // the Q / dO tiles of pair i + 2 are copied from memory straight into the
 // buffer pair i has released (buffer loads with an LDS destination, so no
-// registers are held for them); lse / Delta pass through registers.  Both go
-// out before the atomics of pair i, so they never queue behind them.
+// registers are held for them); at D = 64 lse / Delta pass through
+// registers.  All of them go out before the atomics of pair i, so they never
+// queue behind them.
 // Transposed operands (dO, Q for dV / dK; dS, K for dQ) come from gfx950's
 // transposing LDS read, and dS is stored key-major with 8-byte writes.  All
 // LDS patterns are bank-conflict free under the measured bank model
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   const int wk_lo = kv0 + 32 * kKT * w;
 
   // Prefetch: Q / dO of a pair go straight into LDS (buffer_load ... lds);
-  // lse / Delta pass through registers.
+  // lse / Delta too at D = 128, through registers otherwise.
   float plse = 0.0f, pdlt = 0.0f;
   int prows = 0;
   auto load_pair = [&](int i, int buf) {
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
       // -- P = exp2(S scale log2e - lse log2e); dS' = P (dP - Delta).  The
       //    factor `scale` of dS is applied once to dK (epilogue) and to dQ
       //    (postprocess), not per element.  Masks only on tiles that need them:
-      //    visible iff lo <= q - k <= hi and k < L.
+      //    visible iff lo <= q - k <= hi, k < L and q < L.
       const bool full = (q0 + BM <= L) && (tk_hi < L) && (!p.causal || tk_hi <= q0) &&
                         (p.window <= 0 || tk_lo > q0 + BM - 1 - p.window);
       const int kj = tk_lo + n;
@@ -400,8 +401,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
         }
     }
 
-    // -- next pair's Q / dO / lse / Delta into the other buffer; loads for
-    //    the pair after it go out before this pair's atomics.
+    // -- next pair's lse / Delta into the other buffer (register path); the
+    //    copies for the pair after it go out before this pair's atomics.
     if (i + 1 < npairs) store_pair(buf ^ 1);
     // The copies for pair i + 1 must have landed: after them this wave
     // issued the two lse / Delta register loads (unless those are copies

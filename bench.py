@@ -150,10 +150,21 @@ def prepost_bytes(x: dict) -> tuple:
     return pre, post
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank lines (string literals in these
+    files hold no comment markers)."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def _source_hash() -> str:
+    """Hash of the main kernel's code (comments and blank lines ignored)."""
     h = hashlib.sha256()
     for f in (BWD_SOURCE, os.path.join(os.path.dirname(BWD_SOURCE), "common.h")):
-        h.update(open(f, "rb").read())
+        h.update(_code_only(open(f).read()).encode())
     return h.hexdigest()[:16]
 
 
