@@ -42,6 +42,29 @@ struct FwdCfg {
   static_assert(2 * BYTES <= 160 * 1024, "two workgroups per CU");
 };
 
+// acc + the sum of the 8 values, two per v_dot2_f32_{f16,bf16} (products
+// with 1 are exact; accumulation in fp32).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float sum8(f16x8 v, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 pr = {v[2 * i], v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2(pr, one, acc, false);
+  }
+  return acc;
+}
+__device__ __forceinline__ float sum8(bf16x8 v, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pr = {v[2 * i], v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
+}
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -201,17 +224,10 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
       const float m_new = fmaxf(m_run, mraw * p.scale_log2);
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;
       const float alpha = fast_exp2(m_run - m_use);
-      float lsum = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(st[mt][r] * p.scale_log2 - m_use);
-          st[mt][r] = pv;
-          lsum += pv;
-        }
-      lsum += xor32(lsum);
-      l_run = l_run * alpha + lsum;
+        for (int r = 0; r < 16; ++r) st[mt][r] = fast_exp2(st[mt][r] * p.scale_log2 - m_use);
       // alpha is exactly 1 on lanes whose maximum did not move; skip the
       // rescale when that holds for the whole wave.
       if (!__all(m_new == m_run)) {
@@ -223,10 +239,14 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
       // O^T += V^T P^T over the 64 keys in four 16-key steps.  Slot (c, e)
       // of step ks holds key 16 ks + (e / 4) * 8 + 4 c + e % 4, which is
       // where the C layout of S^T already keeps it; the transposing read of
-      // the row-major V tile delivers the A operand in the same order.
+      // the row-major V tile delivers the A operand in the same order.  The
+      // row sum is taken over the same rounded P (two per dot2 instruction,
+      // fp32 accumulation), so the weights of O sum to one.
+      float lsum = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < kFwdBN / 16; ++ks) {
         const T8 pb = pack8<T>(st[ks >> 1], 8 * (ks & 1));
+        lsum = sum8(pb, lsum);
         const int row = 16 * ks + 4 * c + (l16 >> 2);
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
@@ -234,6 +254,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
           oacc[t] = mfma32(tr_pair<T>(vt, rm_off<D>(row, col), rm_off<D>(row + 8, col)), pb, oacc[t]);
         }
       }
+      lsum += xor32(lsum);
+      l_run = l_run * alpha + lsum;
     }
     // The next block's copies have landed and every wave is done with this
     // stage before it is overwritten.
