@@ -55,24 +55,40 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o,
 }
 
 // One workgroup per query head: dsink[h] = -sum_t exp(sink[h] - lse[h][t]) * delta[h][t],
-// reduced in a fixed order (per-thread strided sums, then a fixed tree), so
-// the result is deterministic and needs neither atomics nor prior zeroing.
-__global__ __launch_bounds__(256) void dsink_kernel(const float* __restrict__ lse,
-                                                    const float* __restrict__ delta,
-                                                    const float* __restrict__ sink,
-                                                    float* __restrict__ dsink, int total) {
-  __shared__ float part[4];
+// reduced in a fixed order (per-thread strided sums over four independent
+// accumulators, then fixed trees across lanes and waves), so the result is
+// deterministic and needs neither atomics nor prior zeroing.
+constexpr int kDsinkThreads = 1024;
+__global__ __launch_bounds__(kDsinkThreads) void dsink_kernel(const float* __restrict__ lse,
+                                                              const float* __restrict__ delta,
+                                                              const float* __restrict__ sink,
+                                                              float* __restrict__ dsink, int total) {
+  __shared__ float part[kDsinkThreads / 64];
   const int h = blockIdx.x;
   const float s = sink[h];
   const float* l = lse + (size_t)h * total;
   const float* dl = delta + (size_t)h * total;
-  float acc = 0.0f;
-  for (int t = threadIdx.x; t < total; t += 256) acc += expf(s - l[t]) * dl[t];
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int t = threadIdx.x;
+  for (; t + 3 * kDsinkThreads < total; t += 4 * kDsinkThreads) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    for (int u = 0; u < 4; ++u) {
+      const int tu = t + u * kDsinkThreads;
+      acc[u] += expf(s - l[tu]) * dl[tu];
+    }
+  }
+  for (; t < total; t += kDsinkThreads) acc[0] += expf(s - l[t]) * dl[t];
+  float a = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) a += __shfl_xor(a, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = a;
   __syncthreads();
-  if (threadIdx.x == 0) dsink[h] = -((part[0] + part[1]) + (part[2] + part[3]));
+  if (threadIdx.x == 0) {
+    float r = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kDsinkThreads / 64; i += 2) r += part[i] + part[i + 1];
+    dsink[h] = -r;
+  }
 }
 
 // dq[i] = RNE(scale * dq_accum[i]) for 8 consecutive elements per thread
@@ -106,8 +122,8 @@ static hipError_t preprocess_t(const Problem& p, const void* o, const void* dout
     if (e != hipSuccess) return e;
   }
   if (sink == nullptr) return hipSuccess;
-  hipLaunchKernelGGL(dsink_kernel, dim3(p.hq), dim3(256), 0, stream, lse, delta, sink, dsink,
-                     p.total);
+  hipLaunchKernelGGL(dsink_kernel, dim3(p.hq), dim3(kDsinkThreads), 0, stream, lse, delta, sink,
+                     dsink, p.total);
   return hipGetLastError();
 }
 
