@@ -78,6 +78,9 @@ EDGE = [
     ("zero_length_seq", ai.workload("varlen_gqa").with_(draw_lengths=None, seqlens=(0, 70, 0, 5),
                                                         hq=4, hkv=2)),
     ("exact_tiles", ai.workload("long_gqa").with_(seqlens=(256, 128), hq=8, hkv=2)),
+    ("one_past_tiles", ai.workload("long_gqa").with_(seqlens=(257, 33), hq=8, hkv=2)),
+    ("d128_noncausal_sink_bf16", ai.workload("tiny_gqa").with_(seqlens=(97, 160), d=128,
+                                                               sink=True, dtype="bf16")),
 ]
 
 
