@@ -135,6 +135,26 @@ def copy_reference_gbs(mib: int = 1024) -> float:
     return 2.0 * n * 4 / (ms * 1e-3) / 1e9
 
 
+def bwd_flops_nominal(x: dict) -> float:
+    """The stated formula without the window: 10 * Hq * D * sum(L^2) / 2 for
+    causal (reported beside the visible-pair count for windowed workloads)."""
+    y = dict(x)
+    y["window"] = 0
+    return bwd_flops(y)
+
+
+def device_info() -> dict:
+    import torch
+
+    pr = torch.cuda.get_device_properties(0)
+    info = {"name": pr.name, "compute_units": pr.multi_processor_count,
+            "arch": getattr(pr, "gcnArchName", "")}
+    clk = getattr(pr, "clock_rate", None)
+    if clk:
+        info["max_clock_mhz"] = round(clk / 1000.0)
+    return info
+
+
 def fwd_flops(x: dict) -> float:
     return bwd_flops(x) * 4.0 / 10.0
 
@@ -347,6 +367,7 @@ def main(argv=None) -> int:
                     "note": "device-scope fp32 atomic adds resolve beyond L2 on this part; "
                             "their device-wide rate, not the MFMA peak, bounds this kernel"},
         "wall_ms_per_step": round(r["wall_ms_per_step"], 4),
+        "device": device_info(),
     }
     base = PAGES_BASELINE.get((w.name, args.n if w.name == "mha_causal" else None))
     if base:
@@ -372,6 +393,9 @@ def main(argv=None) -> int:
                           "atomic_gbs": round(bwd_atomic_bytes(xx) / (rr["bwd_ms"] * 1e-3) / 1e9, 1),
                           "fwd_tflops": round(fwd_flops(xx) / (rr["fwd_ms"] * 1e-3) / 1e12, 2),
                           "attn_fwd_ms": round(rr["fwd_ms"], 4)}
+            if xx["window"] > 0:
+                extra[key]["attn_bwd_kernel_tflops_nominal_formula"] = round(
+                    bwd_flops_nominal(xx) / (rr["bwd_ms"] * 1e-3) / 1e12, 2)
             print(f"bench: {key}: {extra[key]}", file=sys.stderr, flush=True)
         line["per_workload"] = extra
     if not args.no_cpu_baseline:
