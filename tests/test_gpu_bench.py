@@ -1,0 +1,36 @@
+"""The benchmark script on the GPU: its one-line JSON contract and the two
+live reference measurements it takes (fp32 atomic ceiling, plain copy)."""
+import json
+
+import pytest
+
+import bench
+
+pytestmark = pytest.mark.gpu
+
+
+def test_reference_measurements_are_sane():
+    ceiling = bench.atomic_ceiling_gbs()
+    assert ceiling is not None and 200.0 < ceiling < 8000.0
+    copy = bench.copy_reference_gbs(256)
+    assert 500.0 < copy < 8000.0
+
+
+def test_bench_line_contract(capsys):
+    rc = bench.main(["--steps", "2", "--warmup", "1", "--no-extra", "--no-cpu-baseline",
+                     "--workload", "sink_window"])
+    assert rc == 0
+    line = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "atomics"):
+        assert key in line, key
+    assert line["n_gpus"] == 1 and line["steps"] == 2 and line["value"] > 0
+    assert line["config"]["workload"] == "sink_window"
+    r = line["roofline"]
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
+    assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], rel=1e-3)
+    a = line["atomics"]
+    assert a["bytes_per_launch"] == bench.bwd_atomic_bytes(
+        dict(lengths=[4096, 4096], hq=64, hkv=8, d=128, causal=True, window=128))
+    assert 0 < a["achieved_gbs"] < 2 * a["ceiling_gbs"]
