@@ -26,7 +26,9 @@
 //    layout conversion before the atomics, vectorised updates).
 //    Device-scope fp32 atomics resolve at the memory side on this part, so
 //    their bytes per FLOP (4 * BM * D per 10 * BM * BN * D) set a ceiling;
-//    256 keys per workgroup halve them relative to 128.
+//    256 keys per workgroup halve them relative to 128.  At D = 64 the
+//    atomics of a pair are issued during the next pair's tile rather than in
+//    one burst, which keeps the memory-side queue fed more evenly.
 //
 // Data movement.  K is staged once into LDS (needed as the dQ operand); V
 // (and K for D = 64) of the wave live in registers as MFMA B operands.  At
@@ -270,6 +272,20 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   const int g64 = lane >> 4;  // 16-lane group = k-slot group of the 16x16x32 operands
   const uint32_t dq_lane_off = ((16 * dq_qt + 4 * g64) * q_row + 16 * dq_dt + l16) * 4;
 
+  // D = 64: the atomics of pair i leave during the tile of pair i + 1 (half
+  // after its S / dP products, half after the exponentials) instead of as
+  // one burst after the dQ product.
+  constexpr bool TRICKLE = D == 64 && !WIN;
+  f32x4 pend0 = f32x4{}, pend1 = f32x4{};
+  rsrc_t pend_r = make_rsrc(p.dq_accum, 0);
+  auto flush = [&](int lo, int hi) {
+#pragma unroll
+    for (int r = lo; r < hi; ++r) {
+      buf_atomic_add(pend_r, dq_lane_off + r * q_row * 4, pend0[r]);
+      buf_atomic_add(pend_r, dq_lane_off + r * q_row * 4 + 64, pend1[r]);
+    }
+  };
+
   for (int i = 0; i < npairs; ++i) {
     const int buf = i & 1;
     const int h = g * G + i / nq;
@@ -284,9 +300,17 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     for (int kt = 0; kt < kKT; ++kt) {
       // Keys [tk_lo, tk_lo + 32) of this wave's tile kt against queries [q0, q0 + BM).
       const int tk_lo = wk_lo + 32 * kt, tk_hi = tk_lo + 31;
+      // Every path through the tile issues all 8 pending atomics of the
+      // previous pair (the barrier's wait count relies on it).
+      if constexpr (TRICKLE) {
+        if (kt == 0 && i > 0) flush(0, 2);
+      }
       const bool empty = tk_lo >= L || q0 >= L || (p.causal && tk_lo > q0 + BM - 1) ||
                          (p.window > 0 && tk_hi <= q0 - p.window);
       if (empty) {
+        if constexpr (TRICKLE) {
+          if (kt == 0 && i > 0) flush(2, 4);
+        }
         // With WIN the dQ product below skips exactly the key tiles that no
         // query of the block can see, so their dS rows are never read;
         // otherwise they are zeroed.
@@ -350,6 +374,13 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
             sacc[mt][r] = pv;
             pacc[mt][r] = pv * (pacc[mt][r] - d4[e]);
           }
+        }
+      }
+      if constexpr (TRICKLE) {
+        if (kt == 0 && i > 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          flush(2, 4);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // Edge tiles: zero P and dS where the key is hidden.  Selecting (not
@@ -458,13 +489,20 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     {
       const int rows = uni(min(L - q0, BM));
       const rsrc_t dq = make_rsrc(p.dq_accum + ((size_t)(a + q0) * p.hq + h) * D, rows * q_row * 4);
+      if constexpr (TRICKLE) {
+        pend0 = qacc0;
+        pend1 = qacc1;
+        pend_r = dq;
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        buf_atomic_add(dq, dq_lane_off + r * q_row * 4, qacc0[r]);
-        buf_atomic_add(dq, dq_lane_off + r * q_row * 4 + 64, qacc1[r]);
+        for (int r = 0; r < 4; ++r) {
+          buf_atomic_add(dq, dq_lane_off + r * q_row * 4, qacc0[r]);
+          buf_atomic_add(dq, dq_lane_off + r * q_row * 4 + 64, qacc1[r]);
+        }
       }
     }
   }
+  if constexpr (TRICKLE) flush(0, 4);
 
   // ---- single write of dK and dV (C layout: column = dim, row = key) -------
   const rsrc_t dkr = make_rsrc(static_cast<T*>(p.dk) + kv_base, nkeys * kv_row * 2);
