@@ -10,7 +10,10 @@ patterns and the SQ_LDS_BANK_CONFLICT counter, which it reproduces exactly):
 64 banks of 4 bytes; 16-byte accesses are resolved in passes of 16 lanes,
 8-byte accesses and transposing reads (ds_read_b64_tr_b16) in passes of 32
 lanes; a pass costs one extra cycle per additional distinct dword mapped to
-its busiest bank.  The formulas below mirror chunk_swz (csrc/common.h) and
+its busiest bank.  (Measured for reads; 8-byte stores of the transposed dS
+tile cost 4 extra cycles each on the hardware although the model predicts
+none, so the store checks below hold only under the model.)  The formulas
+below mirror chunk_swz (csrc/common.h) and
 slot_swz (csrc/bwd.hip).  The forward kernel uses the same row-major tiles
 for its 64-key K and V blocks.
 """
