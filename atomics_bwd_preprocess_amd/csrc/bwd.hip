@@ -114,12 +114,14 @@ struct BwdArgs {
 };
 
 // Key-major dS tile (BM queries per row): 8-byte slot s of row r lives at
-// slot s ^ slot_swz(r).
+// slot s ^ slot_swz(r).  The 8-byte stores resolve 16 lanes (16 consecutive
+// rows) at a time over 32 banks, so slot_swz is a bijection on the low row
+// bits; the transposing reads need its top two bits to separate rows r,
+// r + 2, r + 8 and r + 10 (both measured on MI355X).
 template <int BM>
 __device__ __forceinline__ int slot_swz(int r) {
-  return BM == 32 ? ((((r >> 3) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 4) & 1))
-                  : ((((r >> 3) & 1) << 3) | (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) |
-                     ((r >> 4) & 1));
+  return BM == 32 ? ((((r >> 3) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 1) & 1))
+                  : ((((r >> 3) & 1) << 3) | (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | (r & 1));
 }
 template <int BM>
 __device__ __forceinline__ int dst_off(int r, int q) {  // q: multiple of 4
