@@ -21,6 +21,8 @@ __all__ = [
     "attn_bwd_preprocess",
     "attn_bwd",
     "attn_bwd_postprocess",
+    "attn_bwd_dkdv",
+    "attn_bwd_dq",
     "attn_abi_version",
     "LIB_PATH",
 ]
@@ -80,6 +82,8 @@ def lib() -> ctypes.CDLL:
             "attn_bwd_preprocess": [S, P, P, P, P, P, P, P, P, P],
             "attn_bwd": [S, P, P, P, P, P, P, P, P, P, P, P],
             "attn_bwd_postprocess": [S, P, P, P],
+            "attn_bwd_dkdv": [S, P, P, P, P, P, P, P, P, P, P],
+            "attn_bwd_dq": [S, P, P, P, P, P, P, P, P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -175,7 +179,8 @@ def attn_fwd(shape: Shape, q, k, v, cu_seqlens, sink, o, lse, stream=None) -> No
 
 def attn_bwd_preprocess(shape: Shape, o, dout, lse, cu_seqlens, sink, delta, dq_accum, dsink,
                         stream=None) -> None:
-    """Delta = rowsum(O * dO) [Hq,T]; dq_accum := 0; dsink [Hq] if a sink is given."""
+    """Delta = rowsum(O * dO) [Hq,T]; dq_accum := 0 unless it is None; dsink [Hq] if a sink
+    is given."""
     import torch
 
     T, Hq, Hkv, D, dt = _dims(shape)
@@ -184,7 +189,7 @@ def attn_bwd_preprocess(shape: Shape, o, dout, lse, cu_seqlens, sink, delta, dq_
     _need(lse, "lse", torch.float32, (Hq, T), allow_none=sink is None)
     _need(sink, "sink", torch.float32, (Hq,), allow_none=True)
     _need(delta, "delta", torch.float32, (Hq, T))
-    _need(dq_accum, "dq_accum", torch.float32, (T, Hq, D))
+    _need(dq_accum, "dq_accum", torch.float32, (T, Hq, D), allow_none=True)
     _need(dsink, "dsink", torch.float32, (Hq,), allow_none=True)
     _check(lib().attn_bwd_preprocess(ctypes.byref(shape), _ptr(o), _ptr(dout), _ptr(lse),
                                      _cu(shape, cu_seqlens), _ptr(sink), _ptr(delta),
@@ -220,3 +225,39 @@ def attn_bwd_postprocess(shape: Shape, dq_accum, dq, stream=None) -> None:
     _need(dq, "dq", dt, (T, Hq, D))
     _check(lib().attn_bwd_postprocess(ctypes.byref(shape), _ptr(dq_accum), _ptr(dq),
                                       _stream(stream)))
+
+
+def attn_bwd_dkdv(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dk, dv,
+                  stream=None) -> None:
+    """Main backward without its dQ product: writes dk, dv (no atomics)."""
+    import torch
+
+    T, Hq, Hkv, D, dt = _dims(shape)
+    _need(q, "q", dt, (T, Hq, D))
+    _need(k, "k", dt, (T, Hkv, D))
+    _need(v, "v", dt, (T, Hkv, D))
+    _need(dout, "dout", dt, (T, Hq, D))
+    _need(lse, "lse", torch.float32, (Hq, T))
+    _need(delta, "delta", torch.float32, (Hq, T))
+    _need(dk, "dk", dt, (T, Hkv, D))
+    _need(dv, "dv", dt, (T, Hkv, D))
+    _check(lib().attn_bwd_dkdv(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                               _ptr(lse), _ptr(delta), _cu(shape, cu_seqlens), _ptr(dk), _ptr(dv),
+                               _stream(stream)))
+
+
+def attn_bwd_dq(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dq, stream=None) -> None:
+    """Query-stationary dQ: writes dq once in the storage dtype (no atomics)."""
+    import torch
+
+    T, Hq, Hkv, D, dt = _dims(shape)
+    _need(q, "q", dt, (T, Hq, D))
+    _need(k, "k", dt, (T, Hkv, D))
+    _need(v, "v", dt, (T, Hkv, D))
+    _need(dout, "dout", dt, (T, Hq, D))
+    _need(lse, "lse", torch.float32, (Hq, T))
+    _need(delta, "delta", torch.float32, (Hq, T))
+    _need(dq, "dq", dt, (T, Hq, D))
+    _check(lib().attn_bwd_dq(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                             _ptr(lse), _ptr(delta), _cu(shape, cu_seqlens), _ptr(dq),
+                             _stream(stream)))

@@ -118,7 +118,7 @@ attn_status_t attn_bwd_preprocess(const attn_shape_t* shape, const void* o, cons
   if (st != ATTN_OK) return st;
   REQUIRE_TENSOR(o);
   REQUIRE_TENSOR(dout);
-  REQUIRE_TENSOR(dq_accum);
+  if (dq_accum) REQUIRE(aligned(dq_accum, 16), "dq_accum is not 16-byte aligned");
   REQUIRE_F32(delta);
   REQUIRE((sink == nullptr) == (dsink == nullptr), "sink and dsink must both be NULL or both set");
   if (sink) {
@@ -153,6 +153,44 @@ attn_status_t attn_bwd(const attn_shape_t* shape, const void* q, const void* k, 
   return hip_status(attn::launch_bwd(p, q, k, v, dout, lse, delta, cu_seqlens, dq_accum, dk, dv,
                                      stream),
                     "attn_bwd");
+}
+
+attn_status_t attn_bwd_dkdv(const attn_shape_t* shape, const void* q, const void* k,
+                            const void* v, const void* dout, const float* lse,
+                            const float* delta, const int32_t* cu_seqlens, void* dk, void* dv,
+                            hipStream_t stream) {
+  attn::Problem p;
+  attn_status_t st = check_shape(shape, cu_seqlens, true, p);
+  if (st != ATTN_OK) return st;
+  REQUIRE_TENSOR(q);
+  REQUIRE_TENSOR(k);
+  REQUIRE_TENSOR(v);
+  REQUIRE_TENSOR(dout);
+  REQUIRE_F32(lse);
+  REQUIRE_F32(delta);
+  REQUIRE_TENSOR(dk);
+  REQUIRE_TENSOR(dv);
+  if (p.total == 0) return ok();
+  return hip_status(attn::launch_bwd_dkdv(p, q, k, v, dout, lse, delta, cu_seqlens, dk, dv, stream),
+                    "attn_bwd_dkdv");
+}
+
+attn_status_t attn_bwd_dq(const attn_shape_t* shape, const void* q, const void* k, const void* v,
+                          const void* dout, const float* lse, const float* delta,
+                          const int32_t* cu_seqlens, void* dq, hipStream_t stream) {
+  attn::Problem p;
+  attn_status_t st = check_shape(shape, cu_seqlens, true, p);
+  if (st != ATTN_OK) return st;
+  REQUIRE_TENSOR(q);
+  REQUIRE_TENSOR(k);
+  REQUIRE_TENSOR(v);
+  REQUIRE_TENSOR(dout);
+  REQUIRE_F32(lse);
+  REQUIRE_F32(delta);
+  REQUIRE_TENSOR(dq);
+  if (p.total == 0) return ok();
+  return hip_status(attn::launch_bwd_dq(p, q, k, v, dout, lse, delta, cu_seqlens, dq, stream),
+                    "attn_bwd_dq");
 }
 
 attn_status_t attn_bwd_postprocess(const attn_shape_t* shape, const float* dq_accum, void* dq,

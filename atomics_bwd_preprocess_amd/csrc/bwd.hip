@@ -130,7 +130,9 @@ __device__ __forceinline__ int dst_off(int r, int q) {  // q: multiple of 4
 
 // WIN: sliding-window problems, where most key tiles of a query block are
 // invisible; the dQ product then runs only over the visible key tiles.
-template <typename T, int D, bool WIN>
+// DQ: false builds the pass without its dQ product (dK / dV only, for use
+// with the query-stationary dQ pass): no dS tile in LDS, no atomics.
+template <typename T, int D, bool WIN, bool DQ>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   using C = Cfg<D>;
   using T8 = typename V8<T>::type;
@@ -165,12 +167,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   const rsrc_t kr = make_rsrc(static_cast<const T*>(p.k) + kv_base, nkeys * kv_row * 2);
   const rsrc_t vr = make_rsrc(static_cast<const T*>(p.v) + kv_base, nkeys * kv_row * 2);
 
-  // ---- K block into LDS ------------------------------------------------------
+  // ---- K block into LDS (the dQ operand, and the S operand at D = 128) -------
+  if constexpr (DQ || !C::KREG) {
 #pragma unroll 4
-  for (int u = tid; u < kBN * C::CH; u += kThreads) {
-    const int r = u / C::CH, ch = u % C::CH;
-    *reinterpret_cast<u32x4*>(smem + C::K_OFF + rm_off<D>(r, 8 * ch)) =
-        buf_load16(kr, (r * kv_row + 8 * ch) * 2);
+    for (int u = tid; u < kBN * C::CH; u += kThreads) {
+      const int r = u / C::CH, ch = u % C::CH;
+      *reinterpret_cast<u32x4*>(smem + C::K_OFF + rm_off<D>(r, 8 * ch)) =
+          buf_load16(kr, (r * kv_row + 8 * ch) * 2);
+    }
   }
   // ---- V (and K for D = 64) of this wave's keys as MFMA B operands ---------
   T8 vreg[kKT][C::VREG];
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   // D = 64: the atomics of pair i leave during the tile of pair i + 1 (half
   // after its S / dP products, half after the exponentials) instead of as
   // one burst after the dQ product.
-  constexpr bool TRICKLE = D == 64 && !WIN;
+  constexpr bool TRICKLE = DQ && D == 64 && !WIN;
   f32x4 pend0 = f32x4{}, pend1 = f32x4{};
   rsrc_t pend_r = make_rsrc(p.dq_accum, 0);
   auto flush = [&](int lo, int hi) {
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
         // With WIN the dQ product below skips exactly the key tiles that no
         // query of the block can see, so their dS rows are never read;
         // otherwise they are zeroed.
-        if constexpr (!WIN) {
+        if constexpr (DQ && !WIN) {
           const u32x2 z = {0u, 0u};
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
@@ -427,16 +431,18 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
       }
 
       // -- dS to LDS, key-major: 4 consecutive queries per 8-byte write.
+      if constexpr (DQ) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          T4 v4;
+          for (int g4 = 0; g4 < 4; ++g4) {
+            T4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = to16<T>(pacc[mt][4 * g4 + e]);
-          *reinterpret_cast<u32x2*>(dss + dst_off<BM>(32 * kKT * w + 32 * kt + n, 32 * mt + 8 * g4 + 4 * c)) =
-              __builtin_bit_cast(u32x2, v4);
-        }
+            for (int e = 0; e < 4; ++e) v4[e] = to16<T>(pacc[mt][4 * g4 + e]);
+            *reinterpret_cast<u32x2*>(dss + dst_off<BM>(32 * kKT * w + 32 * kt + n, 32 * mt + 8 * g4 + 4 * c)) =
+                __builtin_bit_cast(u32x2, v4);
+          }
+      }
     }
 
     // -- next pair's lse / Delta into the other buffer (register path); the
@@ -448,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     // (memory operations complete in order).
     {
       constexpr int after = C::LSE_DMA ? 0 : 2;
-      if (i == 0)
+      if (i == 0 || !DQ)
         __builtin_amdgcn_s_waitcnt(kVmcnt0 + after);
       else
         __builtin_amdgcn_s_waitcnt(kVmcnt0 + after + 8);
@@ -456,55 +462,57 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     __syncthreads();
     if (i + 2 < npairs) load_pair(i + 2, buf);
 
-    // -- dQ partial = dS K for this wave's two 16 x 16 tiles.  Slot (g, e)
-    //    of the 16x16x32 operands holds key 32 ks + 8 g + e; k-step ks covers
-    //    the keys of wave ks.  With WIN only the key tiles some query of the
-    //    block can see are visited (exactly the tiles not "empty" above).
-    f32x4 qacc0 = f32x4{}, qacc1 = f32x4{};
-    {
-      int ks_lo = 0, ks_hi = kBN / 32;
-      if constexpr (WIN) {
-        ks_hi = min(ks_hi, (nkeys + 31) / 32);
-        ks_hi = min(ks_hi, (q0 + BM - 1 - kv0) / 32 + 1);  // windows are causal
-        // tile ks is visible iff 32 ks + 31 > q0 - W - kv0, i.e.
-        // ks >= floor((q0 - W + 1 - kv0) / 32) (arithmetic shift = floor).
-        ks_lo = max(0, (q0 - p.window + 1 - kv0) >> 5);
-      }
-      const int qcol = 16 * dq_qt + 4 * (lane & 3);
-      const int dcol = 16 * dq_dt + 4 * (lane & 3);
-      auto step = [&](int ks) {
-        const int key = 32 * ks + 8 * g64 + (l16 >> 2);
-        const T8 as = tr_pair<T>(dss, dst_off<BM>(key, qcol), dst_off<BM>(key + 4, qcol));
-        const T8 b0 = tr_pair<T>(smem, C::K_OFF + rm_off<D>(key, dcol),
-                                 C::K_OFF + rm_off<D>(key + 4, dcol));
-        const T8 b1 = tr_pair<T>(smem, C::K_OFF + rm_off<D>(key, dcol + 16),
-                                 C::K_OFF + rm_off<D>(key + 4, dcol + 16));
-        qacc0 = mfma16(as, b0, qacc0);
-        qacc1 = mfma16(as, b1, qacc1);
-      };
-      // Full unrolling fits the register budget only at D = 64.
-      if constexpr (WIN || D == 128) {
+    if constexpr (DQ) {
+      // -- dQ partial = dS K for this wave's two 16 x 16 tiles.  Slot (g, e)
+      //    of the 16x16x32 operands holds key 32 ks + 8 g + e; k-step ks covers
+      //    the keys of wave ks.  With WIN only the key tiles some query of the
+      //    block can see are visited (exactly the tiles not "empty" above).
+      f32x4 qacc0 = f32x4{}, qacc1 = f32x4{};
+      {
+        int ks_lo = 0, ks_hi = kBN / 32;
+        if constexpr (WIN) {
+          ks_hi = min(ks_hi, (nkeys + 31) / 32);
+          ks_hi = min(ks_hi, (q0 + BM - 1 - kv0) / 32 + 1);  // windows are causal
+          // tile ks is visible iff 32 ks + 31 > q0 - W - kv0, i.e.
+          // ks >= floor((q0 - W + 1 - kv0) / 32) (arithmetic shift = floor).
+          ks_lo = max(0, (q0 - p.window + 1 - kv0) >> 5);
+        }
+        const int qcol = 16 * dq_qt + 4 * (lane & 3);
+        const int dcol = 16 * dq_dt + 4 * (lane & 3);
+        auto step = [&](int ks) {
+          const int key = 32 * ks + 8 * g64 + (l16 >> 2);
+          const T8 as = tr_pair<T>(dss, dst_off<BM>(key, qcol), dst_off<BM>(key + 4, qcol));
+          const T8 b0 = tr_pair<T>(smem, C::K_OFF + rm_off<D>(key, dcol),
+                                   C::K_OFF + rm_off<D>(key + 4, dcol));
+          const T8 b1 = tr_pair<T>(smem, C::K_OFF + rm_off<D>(key, dcol + 16),
+                                   C::K_OFF + rm_off<D>(key + 4, dcol + 16));
+          qacc0 = mfma16(as, b0, qacc0);
+          qacc1 = mfma16(as, b1, qacc1);
+        };
+        // Full unrolling fits the register budget only at D = 64.
+        if constexpr (WIN || D == 128) {
 #pragma unroll 2
-        for (int ks = ks_lo; ks < ks_hi; ++ks) step(ks);
-      } else {
+          for (int ks = ks_lo; ks < ks_hi; ++ks) step(ks);
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < kBN / 32; ++ks) step(ks);
+          for (int ks = 0; ks < kBN / 32; ++ks) step(ks);
+        }
       }
-    }
-    // -- region-wide fp32 atomics straight from the C layout; rows past the
-    //    sequence end fall outside the resource and are dropped.
-    {
-      const int rows = uni(min(L - q0, BM));
-      const rsrc_t dq = make_rsrc(p.dq_accum + ((size_t)(a + q0) * p.hq + h) * D, rows * q_row * 4);
-      if constexpr (TRICKLE) {
-        pend0 = qacc0;
-        pend1 = qacc1;
-        pend_r = dq;
-      } else {
+      // -- region-wide fp32 atomics straight from the C layout; rows past the
+      //    sequence end fall outside the resource and are dropped.
+      {
+        const int rows = uni(min(L - q0, BM));
+        const rsrc_t dq = make_rsrc(p.dq_accum + ((size_t)(a + q0) * p.hq + h) * D, rows * q_row * 4);
+        if constexpr (TRICKLE) {
+          pend0 = qacc0;
+          pend1 = qacc1;
+          pend_r = dq;
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          buf_atomic_add(dq, dq_lane_off + r * q_row * 4, qacc0[r]);
-          buf_atomic_add(dq, dq_lane_off + r * q_row * 4 + 64, qacc1[r]);
+          for (int r = 0; r < 4; ++r) {
+            buf_atomic_add(dq, dq_lane_off + r * q_row * 4, qacc0[r]);
+            buf_atomic_add(dq, dq_lane_off + r * q_row * 4 + 64, qacc1[r]);
+          }
         }
       }
     }
@@ -527,22 +535,21 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
       }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool DQ>
 hipError_t bwd_t(const BwdArgs& args, int nkb, hipStream_t stream) {
   const unsigned blocks = (unsigned)nkb * args.num_seqs * args.hkv;
   if (args.window > 0)
-    hipLaunchKernelGGL((bwd_kernel<T, D, true>), dim3(blocks), dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((bwd_kernel<T, D, true, DQ>), dim3(blocks), dim3(kThreads), 0, stream, args);
   else
-    hipLaunchKernelGGL((bwd_kernel<T, D, false>), dim3(blocks), dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((bwd_kernel<T, D, false, DQ>), dim3(blocks), dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void* v,
-                      const void* dout, const float* lse, const float* delta,
-                      const int32_t* cu, float* dq_accum, void* dk, void* dv,
-                      hipStream_t stream) {
+template <bool DQ>
+hipError_t bwd_dispatch(const Problem& p, const void* q, const void* k, const void* v,
+                        const void* dout, const float* lse, const float* delta,
+                        const int32_t* cu, float* dq_accum, void* dk, void* dv,
+                        hipStream_t stream) {
   BwdArgs a;
   a.q = q;
   a.k = k;
@@ -564,8 +571,24 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
   a.scale = p.scale;
   a.scale_log2 = p.scale * kLog2e;
   const int nkb = (p.max_seqlen + kBN - 1) / kBN;
-  if (p.bf16) return p.d == 64 ? bwd_t<__bf16, 64>(a, nkb, stream) : bwd_t<__bf16, 128>(a, nkb, stream);
-  return p.d == 64 ? bwd_t<_Float16, 64>(a, nkb, stream) : bwd_t<_Float16, 128>(a, nkb, stream);
+  if (p.bf16)
+    return p.d == 64 ? bwd_t<__bf16, 64, DQ>(a, nkb, stream) : bwd_t<__bf16, 128, DQ>(a, nkb, stream);
+  return p.d == 64 ? bwd_t<_Float16, 64, DQ>(a, nkb, stream) : bwd_t<_Float16, 128, DQ>(a, nkb, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void* v,
+                      const void* dout, const float* lse, const float* delta,
+                      const int32_t* cu, float* dq_accum, void* dk, void* dv,
+                      hipStream_t stream) {
+  return bwd_dispatch<true>(p, q, k, v, dout, lse, delta, cu, dq_accum, dk, dv, stream);
+}
+
+hipError_t launch_bwd_dkdv(const Problem& p, const void* q, const void* k, const void* v,
+                           const void* dout, const float* lse, const float* delta,
+                           const int32_t* cu, void* dk, void* dv, hipStream_t stream) {
+  return bwd_dispatch<false>(p, q, k, v, dout, lse, delta, cu, nullptr, dk, dv, stream);
 }
 
 }  // namespace attn

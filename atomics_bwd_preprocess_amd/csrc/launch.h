@@ -29,6 +29,16 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
                       const int32_t* cu, float* dq_accum, void* dk, void* dv,
                       hipStream_t stream);
 
+// Main pass without its dQ product (dK / dV only).
+hipError_t launch_bwd_dkdv(const Problem& p, const void* q, const void* k, const void* v,
+                           const void* dout, const float* lse, const float* delta,
+                           const int32_t* cu, void* dk, void* dv, hipStream_t stream);
+
+// Query-stationary dQ pass (dQ written once in the storage dtype).
+hipError_t launch_bwd_dq(const Problem& p, const void* q, const void* k, const void* v,
+                         const void* dout, const float* lse, const float* delta,
+                         const int32_t* cu, void* dq, hipStream_t stream);
+
 hipError_t launch_postprocess(const Problem& p, const float* dq_accum, void* dq,
                               hipStream_t stream);
 

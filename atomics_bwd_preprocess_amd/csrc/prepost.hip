@@ -4,13 +4,14 @@
 //  * preprocess  (tilelang-ascend PR "GQA Sink Backward BHSD": the merged
 //    preprocess + dsink kernel, and Phase 0 / Phase 5 of its single backward
 //    kernel): Delta = row sum of O * dO in fp32, zeroing of the fp32 dQ
-//    accumulator, and dsink = -sum_t exp(sink - lse) * Delta.
+//    accumulator (when the atomic dQ path uses one), and
+//    dsink = -sum_t exp(sink - lse) * Delta.
 //  * postprocess (same PR: the postprocess kernel that casts the fp32
 //    accumulated gradient to fp16): dQ = RNE cast of scale x the fp32
 //    accumulator (the main pass leaves the score scale out of dS).
 //
 // Algorithmic bytes (e = 2 bytes per 16-bit element, R = T * Hq rows):
-//   delta kernel:  R * D * 2e (O, dO) + R * 4 (Delta) + R * D * 4 (zeroing)
+//   delta kernel:  R * D * 2e (O, dO) + R * 4 (Delta) [+ R * D * 4 (zeroing)]
 //   dsink kernel:  R * 8 (lse, Delta)
 //   postprocess:   R * D * (4 + e)
 #include "common.h"
@@ -21,8 +22,9 @@ namespace attn {
 // One workgroup: query head blockIdx.y, tokens [blockIdx.x * 64, +64).
 // A row (token, head) is D contiguous elements read as 16-byte chunks by
 // D / 8 consecutive lanes; the partial dot products are reduced across those
-// lanes with xor shuffles (which stay inside a row group).
-template <typename T, int D>
+// lanes with xor shuffles (which stay inside a row group).  ZERO: also clear
+// the row of the fp32 dQ accumulator.
+template <typename T, int D, bool ZERO>
 __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o,
                                                     const T* __restrict__ dout,
                                                     float* __restrict__ delta,
@@ -44,9 +46,11 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o,
       const auto b = ld16<T>(dout + base);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc += (float)a[i] * (float)b[i];
-      f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f32x4*>(dq_accum + base) = z;
-      *reinterpret_cast<f32x4*>(dq_accum + base + 4) = z;
+      if constexpr (ZERO) {
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(dq_accum + base) = z;
+        *reinterpret_cast<f32x4*>(dq_accum + base + 4) = z;
+      }
     }
 #pragma unroll
     for (int off = kLanesPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -115,9 +119,14 @@ static hipError_t preprocess_t(const Problem& p, const void* o, const void* dout
                                float* dq_accum, float* dsink, hipStream_t stream) {
   if (p.total > 0) {
     dim3 grid((p.total + 63) / 64, p.hq);
-    hipLaunchKernelGGL((delta_kernel<T, D>), grid, dim3(256), 0, stream,
-                       static_cast<const T*>(o), static_cast<const T*>(dout), delta, dq_accum,
-                       p.total, p.hq);
+    if (dq_accum)
+      hipLaunchKernelGGL((delta_kernel<T, D, true>), grid, dim3(256), 0, stream,
+                         static_cast<const T*>(o), static_cast<const T*>(dout), delta, dq_accum,
+                         p.total, p.hq);
+    else
+      hipLaunchKernelGGL((delta_kernel<T, D, false>), grid, dim3(256), 0, stream,
+                         static_cast<const T*>(o), static_cast<const T*>(dout), delta, dq_accum,
+                         p.total, p.hq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

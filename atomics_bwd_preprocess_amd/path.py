@@ -3,7 +3,9 @@
 ``Workspace`` holds every output and workspace tensor for one problem so
 that repeated steps allocate nothing; ``forward`` / ``backward`` issue the
 library calls in stream order (forward -> preprocess -> main backward ->
-postprocess) with no host synchronisation in between.
+postprocess) with no host synchronisation in between.  ``backward(...,
+deterministic=True)`` runs the atomic-free variant instead (preprocess ->
+dK/dV pass -> query-stationary dQ pass).
 """
 from __future__ import annotations
 
@@ -12,7 +14,8 @@ from typing import Optional
 
 import torch
 
-from . import Shape, attn_bwd, attn_bwd_postprocess, attn_bwd_preprocess, attn_fwd
+from . import (Shape, attn_bwd, attn_bwd_dkdv, attn_bwd_dq, attn_bwd_postprocess,
+               attn_bwd_preprocess, attn_fwd)
 
 DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -82,10 +85,20 @@ def forward(inp: Inputs, ws: Workspace, stream=None) -> None:
     attn_fwd(inp.shape, inp.q, inp.k, inp.v, inp.cu, inp.sink, ws.o, ws.lse, stream)
 
 
-def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None) -> None:
-    """Preprocess -> main backward -> postprocess; O and lse default to ws.o / ws.lse."""
+def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
+             deterministic: bool = False) -> None:
+    """Preprocess -> main backward -> postprocess; O and lse default to ws.o / ws.lse.
+    deterministic: dK/dV pass + query-stationary dQ pass, no atomics (ws.dq_accum unused)."""
     o = ws.o if o is None else o
     lse = ws.lse if lse is None else lse
+    if deterministic:
+        attn_bwd_preprocess(inp.shape, o, inp.do, lse, inp.cu, inp.sink, ws.delta, None,
+                            ws.dsink, stream)
+        attn_bwd_dkdv(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dk,
+                      ws.dv, stream)
+        attn_bwd_dq(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dq,
+                    stream)
+        return
     attn_bwd_preprocess(inp.shape, o, inp.do, lse, inp.cu, inp.sink, ws.delta, ws.dq_accum,
                         ws.dsink, stream)
     attn_bwd(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dq_accum, ws.dk,

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum {
   ATTN_OK = 0,
@@ -100,7 +100,8 @@ attn_status_t attn_fwd(const attn_shape_t* shape, const void* q, const void* k, 
  * kernel; Phase 0 of its single backward kernel computes Delta as the row sum
  * of O*dO; the Dsink kernel computes dsink = -sum exp(sink - lse) * Delta).
  *   delta[h][t]  = sum_d o[t][h][d] * dout[t][h][d]   (fp32 accumulation)
- *   dq_accum     := 0 (all T*Hq*D entries)
+ *   dq_accum     := 0 (all T*Hq*D entries; skipped when dq_accum is NULL,
+ *                   as the deterministic path below needs no accumulator)
  *   dsink[h]     = -sum_t exp(sink[h] - lse[h][t]) * delta[h][t]
  * sink and dsink must both be NULL or both non-NULL.  dsink is written (not
  * accumulated) and its reduction order is fixed, so it is deterministic.
@@ -131,6 +132,30 @@ attn_status_t attn_bwd(const attn_shape_t* shape, const void* q, const void* k, 
                        const void* dout, const float* lse, const float* delta,
                        const int32_t* cu_seqlens, float* dq_accum, void* dk, void* dv,
                        hipStream_t stream);
+
+/*
+ * Deterministic backward, pass 1 of 2: the main pass above without its dQ
+ * product.  Writes dk and dv exactly as attn_bwd does (bitwise the same
+ * values); issues no atomics and needs no dq_accum.
+ */
+attn_status_t attn_bwd_dkdv(const attn_shape_t* shape, const void* q, const void* k,
+                            const void* v, const void* dout, const float* lse,
+                            const float* delta, const int32_t* cu_seqlens, void* dk, void* dv,
+                            hipStream_t stream);
+
+/*
+ * Deterministic backward, pass 2 of 2: query-stationary dQ ([ASC] backward
+ * keeps dQ in the matrix unit's accumulator over its key loop).  Per query
+ * tile it walks the visible key blocks, recomputes S, P, dP and
+ * dS = P o (dP - Delta), accumulates dQ = scale * sum_j dS_ij k_j in fp32
+ * registers and writes dq [T,Hq,D] once (storage dtype, RNE).  No atomics,
+ * no workspace, a fixed summation order: bitwise reproducible.  Same lse
+ * precondition as attn_bwd.  Independent of attn_bwd_dkdv (the two may run
+ * concurrently on different streams).
+ */
+attn_status_t attn_bwd_dq(const attn_shape_t* shape, const void* q, const void* k, const void* v,
+                          const void* dout, const float* lse, const float* delta,
+                          const int32_t* cu_seqlens, void* dq, hipStream_t stream);
 
 /*
  * Backward postprocess ([ASC] postprocess kernel casting the fp32 gradient

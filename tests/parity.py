@@ -64,8 +64,9 @@ def delta_extra(x: dict, o_ref: np.ndarray, dtype: str) -> np.ndarray:
     return 2.0 * UNIT_ROUNDOFF[dtype] * mass
 
 
-def run_gpu(x: dict, device="cuda", o=None, lse=None):
-    """Run forward + backward on the HIP path; returns (inputs, workspace)."""
+def run_gpu(x: dict, device="cuda", o=None, lse=None, deterministic=False):
+    """Run forward + backward on the HIP path; returns (inputs, workspace).
+    deterministic: the atomic-free backward (dK/dV pass + query-stationary dQ)."""
     import torch
 
     from atomics_bwd_preprocess_amd import path
@@ -76,9 +77,9 @@ def run_gpu(x: dict, device="cuda", o=None, lse=None):
     if o is not None:
         o_t = torch.from_numpy(np.ascontiguousarray(o, dtype=np.float32)).to(device).to(inp.q.dtype)
         lse_t = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).to(device)
-        path.backward(inp, ws, o=o_t, lse=lse_t)
+        path.backward(inp, ws, o=o_t, lse=lse_t, deterministic=deterministic)
     else:
-        path.backward(inp, ws)
+        path.backward(inp, ws, deterministic=deterministic)
     torch.cuda.synchronize()
     return inp, ws
 

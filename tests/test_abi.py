@@ -26,15 +26,16 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["attn_fwd", "attn_bwd_preprocess", "attn_bwd",
-                                  "attn_bwd_postprocess", "attn_status_string",
-                                  "attn_last_error", "attn_abi_version"])
+                                  "attn_bwd_postprocess", "attn_bwd_dkdv", "attn_bwd_dq",
+                                  "attn_status_string", "attn_last_error",
+                                  "attn_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
     L = ab.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert ab.attn_abi_version() == 1
+    assert ab.attn_abi_version() == 2
     assert L.attn_status_string(0) == b"ok"
     assert L.attn_status_string(1) == b"invalid argument"
 
@@ -88,6 +89,22 @@ def test_pointer_validation():
                       None) == 1
     # postprocess: misaligned dq
     assert L.attn_bwd_postprocess(ctypes.byref(s), FAKE, FAKE + 2, None) == 1
+    # preprocess: a NULL dq_accum is allowed (no zeroing), a misaligned one is not
+    assert L.attn_bwd_preprocess(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, FAKE, FAKE + 4,
+                                 None, None) == 1
+    assert b"dq_accum" in L.attn_last_error()
+    # deterministic passes: missing dv / misaligned dq / missing delta
+    assert L.attn_bwd_dkdv(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                           None) == 1
+    assert b"dv is NULL" in L.attn_last_error()
+    assert L.attn_bwd_dq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE + 8,
+                         None) == 1
+    assert b"dq is not 16-byte aligned" in L.attn_last_error()
+    assert L.attn_bwd_dq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+                         None) == 1
+    assert b"delta is NULL" in L.attn_last_error()
+    assert L.attn_bwd_dq(ctypes.byref(_shape(head_dim=96)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         None, FAKE, None) == 2
     assert L.attn_bwd_postprocess(None, FAKE, FAKE, None) == 1
 
 
@@ -101,6 +118,10 @@ def test_empty_problem_launches_nothing():
     assert L.attn_bwd_postprocess(ctypes.byref(s), FAKE, FAKE, None) == 0
     assert L.attn_bwd_preprocess(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
                                  None) == 0
+    assert L.attn_bwd_dkdv(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           None) == 0
+    assert L.attn_bwd_dq(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         None) == 0
     assert L.attn_last_error() == b""
 
 

@@ -1,0 +1,79 @@
+"""GPU parity of the deterministic backward: the main pass built without its
+dQ product (attn_bwd_dkdv) plus the query-stationary dQ pass (attn_bwd_dq),
+against the fp64 oracle on the same cases as the atomic path, and against the
+atomic path itself: dK / dV bitwise equal, dQ within the tolerance, and every
+output bitwise repeatable run to run."""
+import numpy as np
+import pytest
+
+import attn_inputs as ai
+from oracle import attention as orc
+
+from parity import assert_close, compare_all, outputs, to64
+from test_gpu_parity import EDGE, REDUCED, _announce, _full_compare, _sampled_compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import atomics_bwd_preprocess_amd as ab
+
+    ab.lib()  # fails loudly when the HIP library is missing
+    yield
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_reduced_workloads(name):
+    _full_compare(REDUCED[name], deterministic=True)
+
+
+@pytest.mark.parametrize("label,w", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(label, w):
+    _full_compare(w, deterministic=True)
+
+
+@pytest.mark.parametrize("w", [
+    ai.workload("varlen_gqa").with_(draw_lengths=None, seqlens=(700, 333, 129), hq=8, hkv=2),
+    ai.workload("mha_causal").with_(seqlens=(640,), hq=4, hkv=4),
+    ai.workload("sink_window").with_(seqlens=(500, 77), hq=8, hkv=2, window=100),
+], ids=["varlen_d128", "causal_d64", "window_sink_d128"])
+def test_against_atomic_path_and_repeatable(w):
+    import torch
+
+    from atomics_bwd_preprocess_amd import path
+
+    x = ai.generate(w, 5)
+    _announce(f"deterministic vs atomic {w.name} lengths={x['lengths']}")
+    inp = path.to_device(x)
+    ws_a = path.workspace(inp)
+    path.forward(inp, ws_a)
+    path.backward(inp, ws_a)
+    ws_d = path.workspace(inp)
+    path.backward(inp, ws_d, o=ws_a.o, lse=ws_a.lse, deterministic=True)
+    torch.cuda.synchronize()
+    # dK / dV come from the same arithmetic in the same order
+    assert torch.equal(ws_d.dk, ws_a.dk) and torch.equal(ws_d.dv, ws_a.dv)
+    assert torch.equal(ws_d.delta, ws_a.delta)
+    if ws_a.dsink is not None:
+        assert torch.equal(ws_d.dsink, ws_a.dsink)
+    assert_close(to64(ws_d.dq), to64(ws_a.dq), "dq det vs atomic", w.dtype)
+    dq0 = ws_d.dq.clone()
+    for _ in range(3):
+        ws_d.dq.zero_()
+        path.backward(inp, ws_d, o=ws_a.o, lse=ws_a.lse, deterministic=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ws_d.dq, dq0)
+        assert torch.equal(ws_d.dk, ws_a.dk) and torch.equal(ws_d.dv, ws_a.dv)
+
+
+def test_full_sink_window():
+    _full_compare(ai.workload("sink_window"), row_chunk=256, deterministic=True)
+
+
+@pytest.mark.parametrize("name", ["mha_causal", "long_gqa", "varlen_gqa"])
+def test_full_size_sampled(name):
+    _sampled_compare(ai.workload(name), deterministic=True)

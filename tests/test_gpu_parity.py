@@ -32,11 +32,12 @@ def _announce(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
-def _full_compare(w, seed=0, row_chunk=2048):
+def _full_compare(w, seed=0, row_chunk=2048, deterministic=False):
     x = ai.generate(w, seed)
     _announce(f"{w.name} lengths={x['lengths'][:8]} hq={w.hq} hkv={w.hkv} d={w.d} {w.dtype} "
-              f"causal={w.causal} window={w.window} sink={w.sink} seed={seed}")
-    _, ws = run_gpu(x)
+              f"causal={w.causal} window={w.window} sink={w.sink} seed={seed} "
+              f"deterministic={deterministic}")
+    _, ws = run_gpu(x, deterministic=deterministic)
     ref = orc.forward_backward(x, row_chunk=row_chunk)
     compare_all(outputs(ws), ref, w.dtype, x)
     return x, ws, ref
@@ -153,13 +154,14 @@ def test_full_varlen_gqa():
     _full_compare(ai.workload("varlen_gqa"), row_chunk=1024)
 
 
-def _sampled_compare(w, n_q=256, n_k=48, seed=0, k_tail=64):
+def _sampled_compare(w, n_q=256, n_k=48, seed=0, k_tail=64, deterministic=False):
     """Sampled dQ/O/lse/Delta rows anywhere; dK/dV rows among the last
     `k_tail` keys of each sequence (their query sets are short under the
     causal mask); exact-sum invariants over all dK / dV rows."""
     x = ai.generate(w, seed)
-    _announce(f"full-size sampled {w.name} lengths={x['lengths'][:4]}... T={x['cu_seqlens'][-1]}")
-    inp, ws = run_gpu(x)
+    _announce(f"full-size sampled {w.name} lengths={x['lengths'][:4]}... T={x['cu_seqlens'][-1]} "
+              f"deterministic={deterministic}")
+    inp, ws = run_gpu(x, deterministic=deterministic)
     got = outputs(ws)
     rng = np.random.default_rng(1234)
     T = int(x["cu_seqlens"][-1])
