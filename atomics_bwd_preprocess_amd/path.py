@@ -3,9 +3,16 @@
 ``Workspace`` holds every output and workspace tensor for one problem so
 that repeated steps allocate nothing; ``forward`` / ``backward`` issue the
 library calls in stream order (forward -> preprocess -> main backward ->
-postprocess) with no host synchronisation in between.  ``backward(...,
-deterministic=True)`` runs the atomic-free variant instead (preprocess ->
-dK/dV pass -> query-stationary dQ pass).
+postprocess) with no host synchronisation in between.
+
+``backward`` has two orientations for dQ:
+  * ``mode="atomic"`` (default): the key/value-stationary main pass sends dQ
+    through region-wide fp32 atomics into an accumulator, cast afterwards;
+  * ``mode="deterministic"``: the same pass without its dQ product, then a
+    query-stationary dQ pass that keeps dQ on chip (no atomics, no
+    accumulator; every output bitwise reproducible);
+  * ``mode="auto"``: whichever of the two ``select_mode`` expects to be faster
+    for the shape (measured crossover on MI355X, see ``select_mode``).
 """
 from __future__ import annotations
 
@@ -36,6 +43,7 @@ class Inputs:
     do: torch.Tensor
     cu: Optional[torch.Tensor]
     sink: Optional[torch.Tensor]
+    lengths: Optional[list] = None  # host copy of the sequence lengths, if known
 
 
 @dataclass
@@ -61,7 +69,8 @@ def to_device(x: dict, device="cuda") -> Inputs:
 
     sink = None if x["sink"] is None else torch.from_numpy(x["sink"]).to(device)
     cu = torch.from_numpy(x["cu_seqlens"]).to(device=device, dtype=torch.int32)
-    return Inputs(shape, dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["do"]), cu, sink)
+    return Inputs(shape, dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["do"]), cu, sink,
+                  [int(n) for n in x["lengths"]])
 
 
 def workspace(inp: Inputs) -> Workspace:
@@ -81,29 +90,72 @@ def workspace(inp: Inputs) -> Workspace:
     )
 
 
+def keys_per_query(shape: Shape, lengths=None) -> float:
+    """Mean number of keys a query sees (the attention work per query row).
+    Exact from the host lengths when given, else from max_seqlen (exact for a
+    dense batch)."""
+    lens = list(lengths) if lengths is not None else [shape.max_seqlen] * shape.num_seqs
+    rows = sum(lens)
+    if rows == 0:
+        return 0.0
+    W = shape.window
+    pairs = 0
+    for n in lens:
+        if not shape.causal:
+            pairs += n * n
+        elif W > 0:
+            m = min(n, W)  # queries 0..m-1 see i + 1 keys, the rest see W
+            pairs += m * (m + 1) // 2 + (n - m) * W
+        else:
+            pairs += n * (n + 1) // 2
+    return pairs / rows
+
+
+def select_mode(shape: Shape, lengths=None) -> str:
+    """"deterministic" (query-stationary dQ) or "atomic", whichever measured
+    faster on MI355X for this kind of shape.  Backward times of both paths
+    (preprocess through dQ), one MI355X:
+      D = 128: query-stationary faster up to ~1.5k keys per query (0.89x at
+      512, 0.90x at 1024, 1.02x at 2048, 1.07x at 4096) and with every window
+      measured (W = 128 .. 2048: 0.88x - 0.98x);
+      D = 64: atomic faster without a window (1.24x at 512 keys per query,
+      1.08x at 1024); with a window query-stationary is faster up to
+      W ~ 1k (0.93x at 128, 0.98x at 512, 1.01x at 2048)."""
+    kq = keys_per_query(shape, lengths)
+    if shape.head_dim == 128:
+        return "deterministic" if (shape.window > 0 or kq <= 1536) else "atomic"
+    return "deterministic" if 0 < shape.window <= 1024 else "atomic"
+
+
 def forward(inp: Inputs, ws: Workspace, stream=None) -> None:
     attn_fwd(inp.shape, inp.q, inp.k, inp.v, inp.cu, inp.sink, ws.o, ws.lse, stream)
 
 
 def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
-             deterministic: bool = False) -> None:
+             mode: str = "atomic") -> str:
     """Preprocess -> main backward -> postprocess; O and lse default to ws.o / ws.lse.
-    deterministic: dK/dV pass + query-stationary dQ pass, no atomics (ws.dq_accum unused)."""
+    mode "deterministic": dK/dV pass + query-stationary dQ pass, no atomics
+    (ws.dq_accum unused); "auto": select_mode.  Returns the mode that ran."""
+    if mode == "auto":
+        mode = select_mode(inp.shape, inp.lengths)
+    if mode not in ("atomic", "deterministic"):
+        raise ValueError(f"unknown backward mode {mode!r}")
     o = ws.o if o is None else o
     lse = ws.lse if lse is None else lse
-    if deterministic:
+    if mode == "deterministic":
         attn_bwd_preprocess(inp.shape, o, inp.do, lse, inp.cu, inp.sink, ws.delta, None,
                             ws.dsink, stream)
         attn_bwd_dkdv(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dk,
                       ws.dv, stream)
         attn_bwd_dq(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dq,
                     stream)
-        return
+        return mode
     attn_bwd_preprocess(inp.shape, o, inp.do, lse, inp.cu, inp.sink, ws.delta, ws.dq_accum,
                         ws.dsink, stream)
     attn_bwd(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dq_accum, ws.dk,
              ws.dv, stream)
     attn_bwd_postprocess(inp.shape, ws.dq_accum, ws.dq, stream)
+    return mode
 
 
 def step(inp: Inputs, ws: Workspace, stream=None) -> None:

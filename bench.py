@@ -7,7 +7,10 @@ attn_bwd_postprocess, all through the C ABI on the current HIP stream.
 convention 2.5 x the forward's 4*B*Hq*N^2*D, halved for causal; sum of L^2
 for varlen; visible pairs for a sliding window) divided by the HIP-event time
 of the three backward launches.  The forward runs in every step (it produces
-O and lse) and is reported separately.
+O and lse) and is reported separately.  The deterministic backward
+(attn_bwd_preprocess without the accumulator -> attn_bwd_dkdv -> attn_bwd_dq,
+no atomics) is timed on the same inputs and reported under "deterministic",
+with the orientation path.select_mode picks for the shape.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--n N] [--seed S] [--no-cpu-baseline] [--no-extra]
@@ -203,8 +206,8 @@ def _traffic(workload: str):
 def run_gpu(x: dict, steps: int, warmup: int) -> dict:
     import torch
 
-    from atomics_bwd_preprocess_amd import (attn_bwd, attn_bwd_postprocess, attn_bwd_preprocess,
-                                            path)
+    from atomics_bwd_preprocess_amd import (attn_bwd, attn_bwd_dkdv, attn_bwd_dq,
+                                            attn_bwd_postprocess, attn_bwd_preprocess, path)
 
     inp = path.to_device(x, "cuda")
     ws = path.workspace(inp)
@@ -234,9 +237,45 @@ def run_gpu(x: dict, steps: int, warmup: int) -> dict:
     out = dict(wall_ms_per_step=1e3 * wall / steps, fwd_ms=float(mean[0]), pre_ms=float(mean[1]),
                bwd_ms=float(mean[2]), post_ms=float(mean[3]),
                bwd_ms_min=float(ms[:, 2].min()), bwd_ms_median=float(np.median(ms[:, 2])))
+    # The deterministic backward on the same inputs: preprocess without the
+    # accumulator, the dK/dV-only main pass, the query-stationary dQ pass.
+    for _ in range(2):
+        path.backward(inp, ws, mode="deterministic")
+    torch.cuda.synchronize()
+    for i in range(steps):
+        e = ev[i]
+        e[0].record(stream)
+        attn_bwd_preprocess(inp.shape, ws.o, inp.do, ws.lse, inp.cu, inp.sink, ws.delta, None,
+                            ws.dsink)
+        e[1].record(stream)
+        attn_bwd_dkdv(inp.shape, inp.q, inp.k, inp.v, inp.do, ws.lse, ws.delta, inp.cu, ws.dk,
+                      ws.dv)
+        e[2].record(stream)
+        attn_bwd_dq(inp.shape, inp.q, inp.k, inp.v, inp.do, ws.lse, ws.delta, inp.cu, ws.dq)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    dm = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(3)] for e in ev]).mean(axis=0)
+    out.update(det_pre_ms=float(dm[0]), dkdv_ms=float(dm[1]), dq_ms=float(dm[2]),
+               auto_mode=path.select_mode(inp.shape, inp.lengths))
     del ws, inp
     torch.cuda.empty_cache()
     return out
+
+
+def deterministic_entry(x: dict, r: dict) -> dict:
+    """Times and rates of the deterministic backward (query-stationary dQ).
+    The dK/dV pass does 8 and the dQ pass 6 of the 10 units of 2*BM*BN*D
+    FLOPs per visible tile pair that the fused pass does."""
+    f = bwd_flops(x)
+    total = r["det_pre_ms"] + r["dkdv_ms"] + r["dq_ms"]
+    return {"bwd_ms": round(total, 4), "bwd_tflops": round(f / (total * 1e-3) / 1e12, 2),
+            "attn_bwd_preprocess_ms": round(r["det_pre_ms"], 4),
+            "attn_bwd_dkdv_ms": round(r["dkdv_ms"], 4),
+            "attn_bwd_dq_ms": round(r["dq_ms"], 4),
+            "attn_bwd_dkdv_tflops": round(0.8 * f / (r["dkdv_ms"] * 1e-3) / 1e12, 2),
+            "attn_bwd_dq_tflops": round(0.6 * f / (r["dq_ms"] * 1e-3) / 1e12, 2),
+            "vs_atomic_path": round((r["pre_ms"] + r["bwd_ms"] + r["post_ms"]) / total, 4),
+            "auto_mode": r["auto_mode"]}
 
 
 def cpu_baseline(x: dict, min_run_s: float = 4.0) -> dict:
@@ -367,6 +406,7 @@ def main(argv=None) -> int:
                     "note": "device-scope fp32 atomic adds resolve beyond L2 on this part; "
                             "their device-wide rate, not the MFMA peak, bounds this kernel"},
         "wall_ms_per_step": round(r["wall_ms_per_step"], 4),
+        "deterministic": deterministic_entry(x, r),
         "device": device_info(),
     }
     base = PAGES_BASELINE.get((w.name, args.n if w.name == "mha_causal" else None))
@@ -393,6 +433,7 @@ def main(argv=None) -> int:
                           "atomic_gbs": round(bwd_atomic_bytes(xx) / (rr["bwd_ms"] * 1e-3) / 1e9, 1),
                           "fwd_tflops": round(fwd_flops(xx) / (rr["fwd_ms"] * 1e-3) / 1e12, 2),
                           "attn_fwd_ms": round(rr["fwd_ms"], 4)}
+            extra[key]["deterministic"] = deterministic_entry(xx, rr)
             if xx["window"] > 0:
                 extra[key]["attn_bwd_kernel_tflops_nominal_formula"] = round(
                     bwd_flops_nominal(xx) / (rr["bwd_ms"] * 1e-3) / 1e12, 2)

@@ -74,12 +74,13 @@ def run_gpu(x: dict, device="cuda", o=None, lse=None, deterministic=False):
     inp = path.to_device(x, device)
     ws = path.workspace(inp)
     path.forward(inp, ws)
+    mode = "deterministic" if deterministic else "atomic"
     if o is not None:
         o_t = torch.from_numpy(np.ascontiguousarray(o, dtype=np.float32)).to(device).to(inp.q.dtype)
         lse_t = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).to(device)
-        path.backward(inp, ws, o=o_t, lse=lse_t, deterministic=deterministic)
+        path.backward(inp, ws, o=o_t, lse=lse_t, mode=mode)
     else:
-        path.backward(inp, ws, deterministic=deterministic)
+        path.backward(inp, ws, mode=mode)
     torch.cuda.synchronize()
     return inp, ws
 

@@ -53,7 +53,7 @@ def test_against_atomic_path_and_repeatable(w):
     path.forward(inp, ws_a)
     path.backward(inp, ws_a)
     ws_d = path.workspace(inp)
-    path.backward(inp, ws_d, o=ws_a.o, lse=ws_a.lse, deterministic=True)
+    path.backward(inp, ws_d, o=ws_a.o, lse=ws_a.lse, mode="deterministic")
     torch.cuda.synchronize()
     # dK / dV come from the same arithmetic in the same order
     assert torch.equal(ws_d.dk, ws_a.dk) and torch.equal(ws_d.dv, ws_a.dv)
@@ -64,7 +64,7 @@ def test_against_atomic_path_and_repeatable(w):
     dq0 = ws_d.dq.clone()
     for _ in range(3):
         ws_d.dq.zero_()
-        path.backward(inp, ws_d, o=ws_a.o, lse=ws_a.lse, deterministic=True)
+        path.backward(inp, ws_d, o=ws_a.o, lse=ws_a.lse, mode="deterministic")
         torch.cuda.synchronize()
         assert torch.equal(ws_d.dq, dq0)
         assert torch.equal(ws_d.dk, ws_a.dk) and torch.equal(ws_d.dv, ws_a.dv)

@@ -34,3 +34,8 @@ def test_bench_line_contract(capsys):
     assert a["bytes_per_launch"] == bench.bwd_atomic_bytes(
         dict(lengths=[4096, 4096], hq=64, hkv=8, d=128, causal=True, window=128))
     assert 0 < a["achieved_gbs"] < 2 * a["ceiling_gbs"]
+    d = line["deterministic"]
+    assert d["auto_mode"] == "deterministic"  # D = 128 with a window
+    assert d["bwd_ms"] == pytest.approx(d["attn_bwd_preprocess_ms"] + d["attn_bwd_dkdv_ms"]
+                                        + d["attn_bwd_dq_ms"], abs=2e-4)
+    assert d["bwd_tflops"] > 0 and d["attn_bwd_dq_tflops"] > 0
