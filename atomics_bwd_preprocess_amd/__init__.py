@@ -31,6 +31,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn_bwd.so")
 
 ATTN_F16, ATTN_BF16 = 0, 1
+ATTN_LAYOUT_THD, ATTN_LAYOUT_BHSD = 0, 1
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_HIP"}
 
 
@@ -54,15 +55,19 @@ class Shape(ctypes.Structure):
         ("window", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
     ]
 
     @classmethod
     def make(cls, *, num_seqs, max_seqlen, total_tokens, hq, hkv, head_dim, causal, window,
-             scale, dtype) -> "Shape":
+             scale, dtype, layout="thd") -> "Shape":
         if not isinstance(dtype, int):
             dtype = _dtype_code(dtype)
+        if not isinstance(layout, int):
+            layout = {"thd": ATTN_LAYOUT_THD, "bhsd": ATTN_LAYOUT_BHSD}[layout]
         return cls(int(num_seqs), int(max_seqlen), int(total_tokens), int(hq), int(hkv),
-                   int(head_dim), int(bool(causal)), int(window), float(scale), int(dtype))
+                   int(head_dim), int(bool(causal)), int(window), float(scale), int(dtype),
+                   int(layout))
 
 
 _lib = None
@@ -154,6 +159,20 @@ def _dims(shape: Shape):
     return T, Hq, Hkv, D, dt
 
 
+def qshape(shape: Shape) -> tuple:
+    """Shape of q, o, dout, dq and dq_accum for the shape's layout."""
+    if shape.layout == ATTN_LAYOUT_BHSD:
+        return (shape.num_seqs, shape.hq, shape.max_seqlen, shape.head_dim)
+    return (shape.total_tokens, shape.hq, shape.head_dim)
+
+
+def kvshape(shape: Shape) -> tuple:
+    """Shape of k, v, dk and dv for the shape's layout."""
+    if shape.layout == ATTN_LAYOUT_BHSD:
+        return (shape.num_seqs, shape.hkv, shape.max_seqlen, shape.head_dim)
+    return (shape.total_tokens, shape.hkv, shape.head_dim)
+
+
 def _cu(shape: Shape, cu_seqlens):
     import torch
 
@@ -167,11 +186,11 @@ def attn_fwd(shape: Shape, q, k, v, cu_seqlens, sink, o, lse, stream=None) -> No
     import torch
 
     T, Hq, Hkv, D, dt = _dims(shape)
-    _need(q, "q", dt, (T, Hq, D))
-    _need(k, "k", dt, (T, Hkv, D))
-    _need(v, "v", dt, (T, Hkv, D))
+    _need(q, "q", dt, qshape(shape))
+    _need(k, "k", dt, kvshape(shape))
+    _need(v, "v", dt, kvshape(shape))
     _need(sink, "sink", torch.float32, (Hq,), allow_none=True)
-    _need(o, "o", dt, (T, Hq, D))
+    _need(o, "o", dt, qshape(shape))
     _need(lse, "lse", torch.float32, (Hq, T))
     _check(lib().attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _cu(shape, cu_seqlens),
                           _ptr(sink), _ptr(o), _ptr(lse), _stream(stream)))
@@ -184,12 +203,12 @@ def attn_bwd_preprocess(shape: Shape, o, dout, lse, cu_seqlens, sink, delta, dq_
     import torch
 
     T, Hq, Hkv, D, dt = _dims(shape)
-    _need(o, "o", dt, (T, Hq, D))
-    _need(dout, "dout", dt, (T, Hq, D))
+    _need(o, "o", dt, qshape(shape))
+    _need(dout, "dout", dt, qshape(shape))
     _need(lse, "lse", torch.float32, (Hq, T), allow_none=sink is None)
     _need(sink, "sink", torch.float32, (Hq,), allow_none=True)
     _need(delta, "delta", torch.float32, (Hq, T))
-    _need(dq_accum, "dq_accum", torch.float32, (T, Hq, D), allow_none=True)
+    _need(dq_accum, "dq_accum", torch.float32, qshape(shape), allow_none=True)
     _need(dsink, "dsink", torch.float32, (Hq,), allow_none=True)
     _check(lib().attn_bwd_preprocess(ctypes.byref(shape), _ptr(o), _ptr(dout), _ptr(lse),
                                      _cu(shape, cu_seqlens), _ptr(sink), _ptr(delta),
@@ -202,15 +221,15 @@ def attn_bwd(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dq_accum, dk, 
     import torch
 
     T, Hq, Hkv, D, dt = _dims(shape)
-    _need(q, "q", dt, (T, Hq, D))
-    _need(k, "k", dt, (T, Hkv, D))
-    _need(v, "v", dt, (T, Hkv, D))
-    _need(dout, "dout", dt, (T, Hq, D))
+    _need(q, "q", dt, qshape(shape))
+    _need(k, "k", dt, kvshape(shape))
+    _need(v, "v", dt, kvshape(shape))
+    _need(dout, "dout", dt, qshape(shape))
     _need(lse, "lse", torch.float32, (Hq, T))
     _need(delta, "delta", torch.float32, (Hq, T))
-    _need(dq_accum, "dq_accum", torch.float32, (T, Hq, D))
-    _need(dk, "dk", dt, (T, Hkv, D))
-    _need(dv, "dv", dt, (T, Hkv, D))
+    _need(dq_accum, "dq_accum", torch.float32, qshape(shape))
+    _need(dk, "dk", dt, kvshape(shape))
+    _need(dv, "dv", dt, kvshape(shape))
     _check(lib().attn_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
                           _ptr(delta), _cu(shape, cu_seqlens), _ptr(dq_accum), _ptr(dk), _ptr(dv),
                           _stream(stream)))
@@ -221,8 +240,8 @@ def attn_bwd_postprocess(shape: Shape, dq_accum, dq, stream=None) -> None:
     import torch
 
     T, Hq, Hkv, D, dt = _dims(shape)
-    _need(dq_accum, "dq_accum", torch.float32, (T, Hq, D))
-    _need(dq, "dq", dt, (T, Hq, D))
+    _need(dq_accum, "dq_accum", torch.float32, qshape(shape))
+    _need(dq, "dq", dt, qshape(shape))
     _check(lib().attn_bwd_postprocess(ctypes.byref(shape), _ptr(dq_accum), _ptr(dq),
                                       _stream(stream)))
 
@@ -233,14 +252,14 @@ def attn_bwd_dkdv(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dk, dv,
     import torch
 
     T, Hq, Hkv, D, dt = _dims(shape)
-    _need(q, "q", dt, (T, Hq, D))
-    _need(k, "k", dt, (T, Hkv, D))
-    _need(v, "v", dt, (T, Hkv, D))
-    _need(dout, "dout", dt, (T, Hq, D))
+    _need(q, "q", dt, qshape(shape))
+    _need(k, "k", dt, kvshape(shape))
+    _need(v, "v", dt, kvshape(shape))
+    _need(dout, "dout", dt, qshape(shape))
     _need(lse, "lse", torch.float32, (Hq, T))
     _need(delta, "delta", torch.float32, (Hq, T))
-    _need(dk, "dk", dt, (T, Hkv, D))
-    _need(dv, "dv", dt, (T, Hkv, D))
+    _need(dk, "dk", dt, kvshape(shape))
+    _need(dv, "dv", dt, kvshape(shape))
     _check(lib().attn_bwd_dkdv(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                                _ptr(lse), _ptr(delta), _cu(shape, cu_seqlens), _ptr(dk), _ptr(dv),
                                _stream(stream)))
@@ -251,13 +270,13 @@ def attn_bwd_dq(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dq, stream=
     import torch
 
     T, Hq, Hkv, D, dt = _dims(shape)
-    _need(q, "q", dt, (T, Hq, D))
-    _need(k, "k", dt, (T, Hkv, D))
-    _need(v, "v", dt, (T, Hkv, D))
-    _need(dout, "dout", dt, (T, Hq, D))
+    _need(q, "q", dt, qshape(shape))
+    _need(k, "k", dt, kvshape(shape))
+    _need(v, "v", dt, kvshape(shape))
+    _need(dout, "dout", dt, qshape(shape))
     _need(lse, "lse", torch.float32, (Hq, T))
     _need(delta, "delta", torch.float32, (Hq, T))
-    _need(dq, "dq", dt, (T, Hq, D))
+    _need(dq, "dq", dt, qshape(shape))
     _check(lib().attn_bwd_dq(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                              _ptr(lse), _ptr(delta), _cu(shape, cu_seqlens), _ptr(dq),
                              _stream(stream)))

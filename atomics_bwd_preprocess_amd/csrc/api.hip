@@ -67,6 +67,15 @@ attn_status_t check_shape(const attn_shape_t* s, const int32_t* cu, bool need_cu
   REQUIRE(s->window >= 0, "window must be >= 0 (got %d)", s->window);
   REQUIRE(s->window == 0 || s->causal, "a sliding window requires causal = 1");
   REQUIRE(isfinite(s->scale) && s->scale > 0.0f, "scale must be finite and > 0");
+  REQUIRE(s->layout == ATTN_LAYOUT_THD || s->layout == ATTN_LAYOUT_BHSD,
+          "layout must be ATTN_LAYOUT_THD or ATTN_LAYOUT_BHSD (got %d)", s->layout);
+  if (s->layout == ATTN_LAYOUT_BHSD) {
+    REQUIRE(cu == nullptr, "the [B, H, S, D] layout is a dense batch: cu_seqlens must be NULL");
+    REQUIRE((long long)s->num_seqs * s->max_seqlen == s->total_tokens,
+            "the [B, H, S, D] layout needs total_tokens == num_seqs * max_seqlen");
+    REQUIRE((long long)s->max_seqlen * s->head_dim < (1LL << 32),
+            "max_seqlen * head_dim must fit 32 bits in the [B, H, S, D] layout");
+  }
   // 64-bit element counts must fit the launch geometry and index math.
   const long long rows = (long long)s->total_tokens * s->hq;
   REQUIRE(rows * s->head_dim < (1LL << 40), "tensor too large");
@@ -86,6 +95,7 @@ attn_status_t check_shape(const attn_shape_t* s, const int32_t* cu, bool need_cu
   p.window = s->window;
   p.scale = s->scale;
   p.bf16 = s->dtype == ATTN_BF16;
+  p.bhsd = s->layout == ATTN_LAYOUT_BHSD;
   return ATTN_OK;
 }
 

@@ -132,7 +132,8 @@ __device__ __forceinline__ int dst_off(int r, int q) {  // q: multiple of 4
 // invisible; the dQ product then runs only over the visible key tiles.
 // DQ: false builds the pass without its dQ product (dK / dV only, for use
 // with the query-stationary dQ pass): no dS tile in LDS, no atomics.
-template <typename T, int D, bool WIN, bool DQ>
+// BHSD: [B, H, S, D] tensors instead of packed [T, H, D].
+template <typename T, int D, bool WIN, bool DQ, bool BHSD>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   using C = Cfg<D>;
   using T8 = typename V8<T>::type;
@@ -157,13 +158,13 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   const int kv0 = jb * kBN;
   if (kv0 >= L) return;
   const int G = p.hq / p.hkv;
-  const uint32_t kv_row = (uint32_t)p.hkv * D;  // elements between key rows
-  const uint32_t q_row = (uint32_t)p.hq * D;    // elements between query rows
+  const uint32_t kv_row = BHSD ? (uint32_t)D : (uint32_t)p.hkv * D;  // elements between key rows
+  const uint32_t q_row = BHSD ? (uint32_t)D : (uint32_t)p.hq * D;     // elements between query rows
   const int nkeys = uni(min(L - kv0, kBN));     // valid keys of this block
 
   // Buffer resources over this block's keys: rows past the sequence end read
   // as zero and their stores are dropped.
-  const size_t kv_base = ((size_t)(a + kv0) * p.hkv + g) * D;
+  const size_t kv_base = row_off<D, BHSD>(a, kv0, g, p.hkv, p.max_seqlen);
   const rsrc_t kr = make_rsrc(static_cast<const T*>(p.k) + kv_base, nkeys * kv_row * 2);
   const rsrc_t vr = make_rsrc(static_cast<const T*>(p.v) + kv_base, nkeys * kv_row * 2);
 
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     const int h = g * G + i / nq;
     const int q0 = (ib0 + i % nq) * BM;
     const int rows = uni(min(L - q0, BM));  // >= 1: query blocks start inside the sequence
-    const size_t qb = ((size_t)(a + q0) * p.hq + h) * D;
+    const size_t qb = row_off<D, BHSD>(a, q0, h, p.hq, p.max_seqlen);
     const rsrc_t qr = make_rsrc(static_cast<const T*>(p.q) + qb, rows * q_row * 2);
     const rsrc_t dr = make_rsrc(static_cast<const T*>(p.dout) + qb, rows * q_row * 2);
 #pragma unroll
@@ -502,7 +503,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
       //    sequence end fall outside the resource and are dropped.
       {
         const int rows = uni(min(L - q0, BM));
-        const rsrc_t dq = make_rsrc(p.dq_accum + ((size_t)(a + q0) * p.hq + h) * D, rows * q_row * 4);
+        const rsrc_t dq = make_rsrc(p.dq_accum + row_off<D, BHSD>(a, q0, h, p.hq, p.max_seqlen),
+                                    rows * q_row * 4);
         if constexpr (TRICKLE) {
           pend0 = qacc0;
           pend1 = qacc1;
@@ -536,12 +538,20 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
 }
 
 template <typename T, int D, bool DQ>
-hipError_t bwd_t(const BwdArgs& args, int nkb, hipStream_t stream) {
+hipError_t bwd_t(const BwdArgs& args, int nkb, bool bhsd, hipStream_t stream) {
   const unsigned blocks = (unsigned)nkb * args.num_seqs * args.hkv;
-  if (args.window > 0)
-    hipLaunchKernelGGL((bwd_kernel<T, D, true, DQ>), dim3(blocks), dim3(kThreads), 0, stream, args);
-  else
-    hipLaunchKernelGGL((bwd_kernel<T, D, false, DQ>), dim3(blocks), dim3(kThreads), 0, stream, args);
+  const dim3 grid(blocks), block(kThreads);
+  if (args.window > 0) {
+    if (bhsd)
+      hipLaunchKernelGGL((bwd_kernel<T, D, true, DQ, true>), grid, block, 0, stream, args);
+    else
+      hipLaunchKernelGGL((bwd_kernel<T, D, true, DQ, false>), grid, block, 0, stream, args);
+  } else {
+    if (bhsd)
+      hipLaunchKernelGGL((bwd_kernel<T, D, false, DQ, true>), grid, block, 0, stream, args);
+    else
+      hipLaunchKernelGGL((bwd_kernel<T, D, false, DQ, false>), grid, block, 0, stream, args);
+  }
   return hipGetLastError();
 }
 
@@ -572,8 +582,10 @@ hipError_t bwd_dispatch(const Problem& p, const void* q, const void* k, const vo
   a.scale_log2 = p.scale * kLog2e;
   const int nkb = (p.max_seqlen + kBN - 1) / kBN;
   if (p.bf16)
-    return p.d == 64 ? bwd_t<__bf16, 64, DQ>(a, nkb, stream) : bwd_t<__bf16, 128, DQ>(a, nkb, stream);
-  return p.d == 64 ? bwd_t<_Float16, 64, DQ>(a, nkb, stream) : bwd_t<_Float16, 128, DQ>(a, nkb, stream);
+    return p.d == 64 ? bwd_t<__bf16, 64, DQ>(a, nkb, p.bhsd, stream)
+                     : bwd_t<__bf16, 128, DQ>(a, nkb, p.bhsd, stream);
+  return p.d == 64 ? bwd_t<_Float16, 64, DQ>(a, nkb, p.bhsd, stream)
+                   : bwd_t<_Float16, 128, DQ>(a, nkb, p.bhsd, stream);
 }
 
 }  // namespace

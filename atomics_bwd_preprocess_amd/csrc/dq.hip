@@ -61,7 +61,8 @@ struct DqArgs {
   float scale, scale_log2;
 };
 
-template <typename T, int D>
+// BHSD: [B, H, S, D] tensors instead of packed [T, H, D].
+template <typename T, int D, bool BHSD>
 __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(DqArgs p) {
   using C = DqCfg<D>;
   using T8 = typename V8<T>::type;
@@ -87,14 +88,14 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(DqArgs p) {
   const int q0 = qb * kDqBM;
   if (q0 >= L) return;
   const int g = h / G;
-  const uint32_t kv_row = (uint32_t)p.hkv * D;  // elements between key rows
-  const uint32_t q_row = (uint32_t)p.hq * D;    // elements between query rows
+  const uint32_t kv_row = BHSD ? (uint32_t)D : (uint32_t)p.hkv * D;  // elements between key rows
+  const uint32_t q_row = BHSD ? (uint32_t)D : (uint32_t)p.hq * D;     // elements between query rows
 
   // This lane's query (B-operand column n of wave w): its Q and dO rows, lse
   // and Delta.  Rows past the sequence end read as zero and get P = 0.
   const int qi = q0 + 32 * w + n;
   const int qrows = uni(min(L - q0, kDqBM));
-  const size_t qbase = ((size_t)(a + q0) * p.hq + h) * D;
+  const size_t qbase = row_off<D, BHSD>(a, q0, h, p.hq, p.max_seqlen);
   const rsrc_t qr = make_rsrc(static_cast<const T*>(p.q) + qbase, qrows * q_row * 2);
   const rsrc_t dr = make_rsrc(static_cast<const T*>(p.dout) + qbase, qrows * q_row * 2);
   T8 qreg[D / 16], dreg[D / 16];
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(DqArgs p) {
   }
   auto issue = [&](int kb, int stage) {
     const int nk = uni(min(L - kb, kDqBN));
-    const size_t base = ((size_t)(a + kb) * p.hkv + g) * D;
+    const size_t base = row_off<D, BHSD>(a, kb, g, p.hkv, p.max_seqlen);
     const rsrc_t kr = make_rsrc(kp + base, nk * kv_row * 2);
     const rsrc_t vr = make_rsrc(vp + base, nk * kv_row * 2);
 #pragma unroll
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(DqArgs p) {
 
   if (qi >= L) return;
   // C layout of dQ^T: register 4 rg + e of tile t = dim 32 t + 8 rg + 4 c + e.
-  T* __restrict__ op = static_cast<T*>(p.dq) + ((size_t)(a + qi) * p.hq + h) * D;
+  T* __restrict__ op = static_cast<T*>(p.dq) + row_off<D, BHSD>(a, qi, h, p.hq, p.max_seqlen);
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
@@ -236,9 +237,12 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(DqArgs p) {
 }
 
 template <typename T, int D>
-hipError_t dq_t(const DqArgs& args, hipStream_t stream) {
+hipError_t dq_t(const DqArgs& args, bool bhsd, hipStream_t stream) {
   const unsigned blocks = (unsigned)args.nqb * args.num_seqs * args.hq;
-  hipLaunchKernelGGL((dq_kernel<T, D>), dim3(blocks), dim3(kDqThreads), 0, stream, args);
+  if (bhsd)
+    hipLaunchKernelGGL((dq_kernel<T, D, true>), dim3(blocks), dim3(kDqThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((dq_kernel<T, D, false>), dim3(blocks), dim3(kDqThreads), 0, stream, args);
   return hipGetLastError();
 }
 
@@ -266,8 +270,9 @@ hipError_t launch_bwd_dq(const Problem& p, const void* q, const void* k, const v
   a.nqb = (p.max_seqlen + kDqBM - 1) / kDqBM;
   a.scale = p.scale;
   a.scale_log2 = p.scale * kLog2e;
-  if (p.bf16) return p.d == 64 ? dq_t<__bf16, 64>(a, stream) : dq_t<__bf16, 128>(a, stream);
-  return p.d == 64 ? dq_t<_Float16, 64>(a, stream) : dq_t<_Float16, 128>(a, stream);
+  if (p.bf16)
+    return p.d == 64 ? dq_t<__bf16, 64>(a, p.bhsd, stream) : dq_t<__bf16, 128>(a, p.bhsd, stream);
+  return p.d == 64 ? dq_t<_Float16, 64>(a, p.bhsd, stream) : dq_t<_Float16, 128>(a, p.bhsd, stream);
 }
 
 }  // namespace attn

@@ -78,7 +78,8 @@ struct FwdArgs {
   float scale_log2;
 };
 
-template <typename T, int D>
+// BHSD: [B, H, S, D] tensors instead of packed [T, H, D].
+template <typename T, int D, bool BHSD>
 __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
   using C = FwdCfg<D>;
   using T8 = typename V8<T>::type;
@@ -106,14 +107,14 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
   const int q0 = qb * kFwdBM;
   if (q0 >= L) return;
   const int g = h / G;
-  const uint32_t kv_row = (uint32_t)p.hkv * D;  // elements between key rows
-  const uint32_t q_row = (uint32_t)p.hq * D;    // elements between query rows
+  const uint32_t kv_row = BHSD ? (uint32_t)D : (uint32_t)p.hkv * D;  // elements between key rows
+  const uint32_t q_row = BHSD ? (uint32_t)D : (uint32_t)p.hq * D;     // elements between query rows
 
   // This lane's query (B-operand column n of wave w); rows past the sequence
   // end read as zero.
   const int qi = q0 + 32 * w + n;
   const int qrows = uni(min(L - q0, kFwdBM));
-  const rsrc_t qr = make_rsrc(static_cast<const T*>(p.q) + ((size_t)(a + q0) * p.hq + h) * D,
+  const rsrc_t qr = make_rsrc(static_cast<const T*>(p.q) + row_off<D, BHSD>(a, q0, h, p.hq, p.max_seqlen),
                               qrows * q_row * 2);
   T8 qreg[D / 16];
 #pragma unroll
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
   }
   auto issue = [&](int kb, int stage) {
     const int nk = uni(min(L - kb, kFwdBN));
-    const size_t base = ((size_t)(a + kb) * p.hkv + g) * D;
+    const size_t base = row_off<D, BHSD>(a, kb, g, p.hkv, p.max_seqlen);
     const rsrc_t kr = make_rsrc(kp + base, nk * kv_row * 2);
     const rsrc_t vr = make_rsrc(vp + base, nk * kv_row * 2);
 #pragma unroll
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
   if (qi >= L) return;
   const bool any = l_run > 0.0f;
   const float inv = any ? 1.0f / l_run : 0.0f;
-  T* __restrict__ op = static_cast<T*>(p.o) + ((size_t)(a + qi) * p.hq + h) * D;
+  T* __restrict__ op = static_cast<T*>(p.o) + row_off<D, BHSD>(a, qi, h, p.hq, p.max_seqlen);
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
@@ -282,9 +283,12 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
 }
 
 template <typename T, int D>
-hipError_t fwd_t(const FwdArgs& args, hipStream_t stream) {
+hipError_t fwd_t(const FwdArgs& args, bool bhsd, hipStream_t stream) {
   const unsigned blocks = (unsigned)args.nqb * args.num_seqs * args.hq;
-  hipLaunchKernelGGL((fwd_kernel<T, D>), dim3(blocks), dim3(kFwdThreads), 0, stream, args);
+  if (bhsd)
+    hipLaunchKernelGGL((fwd_kernel<T, D, true>), dim3(blocks), dim3(kFwdThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, false>), dim3(blocks), dim3(kFwdThreads), 0, stream, args);
   return hipGetLastError();
 }
 
@@ -310,8 +314,9 @@ hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void
   a.causal = p.causal;
   a.nqb = (p.max_seqlen + kFwdBM - 1) / kFwdBM;
   a.scale_log2 = p.scale * kLog2e;
-  if (p.bf16) return p.d == 64 ? fwd_t<__bf16, 64>(a, stream) : fwd_t<__bf16, 128>(a, stream);
-  return p.d == 64 ? fwd_t<_Float16, 64>(a, stream) : fwd_t<_Float16, 128>(a, stream);
+  if (p.bf16)
+    return p.d == 64 ? fwd_t<__bf16, 64>(a, p.bhsd, stream) : fwd_t<__bf16, 128>(a, p.bhsd, stream);
+  return p.d == 64 ? fwd_t<_Float16, 64>(a, p.bhsd, stream) : fwd_t<_Float16, 128>(a, p.bhsd, stream);
 }
 
 }  // namespace attn

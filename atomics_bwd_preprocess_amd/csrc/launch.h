@@ -14,7 +14,21 @@ struct Problem {
   int window;
   float scale;
   bool bf16;
+  bool bhsd;  // [B, H, S, D] tensors (dense batch) instead of packed [T, H, D]
 };
+
+// Element offset of local row i of head h of the sequence that starts at
+// token a, in a tensor with H heads of D elements: packed [T, H, D], or
+// [B, H, S, D] (dense batch, a = b * S).  q, o, dout, dq and dq_accum use
+// the query heads, k, v, dk and dv the kv heads.  Rows of one head are
+// H * D elements apart when packed and D apart in [B, H, S, D].
+template <int D, bool BHSD>
+__host__ __device__ __forceinline__ size_t row_off(int a, int i, int h, int H, int S) {
+  if constexpr (BHSD)
+    return ((size_t)a * H + (size_t)h * S + i) * D;
+  else
+    return ((size_t)(a + i) * H + h) * D;
+}
 
 hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v,
                       const int32_t* cu, const float* sink, void* o, float* lse,

@@ -23,13 +23,16 @@ namespace attn {
 // A row (token, head) is D contiguous elements read as 16-byte chunks by
 // D / 8 consecutive lanes; the partial dot products are reduced across those
 // lanes with xor shuffles (which stay inside a row group).  ZERO: also clear
-// the row of the fp32 dQ accumulator.
+// the row of the fp32 dQ accumulator.  Row (token t, head h) sits at
+// (t - i) * hq * D + i * row + h * head, with i = t % S for [B, H, S, D]
+// tensors (seq_len = S) and i = 0 for packed [T, H, D] ones (seq_len = 0).
 template <typename T, int D, bool ZERO>
 __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o,
                                                     const T* __restrict__ dout,
                                                     float* __restrict__ delta,
                                                     float* __restrict__ dq_accum, int total,
-                                                    int hq) {
+                                                    int hq, int seq_len, uint32_t row,
+                                                    uint32_t head) {
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerPass = 256 / kLanesPerRow;
   constexpr int kTokens = 64;
@@ -41,7 +44,8 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o,
     const int t = blockIdx.x * kTokens + pass * kRowsPerPass + r;
     float acc = 0.0f;
     if (t < total) {
-      const size_t base = ((size_t)t * hq + h) * D + sub * 8;
+      const int i = seq_len ? t % seq_len : 0;
+      const size_t base = (size_t)(t - i) * hq * D + (size_t)i * row + (size_t)h * head + sub * 8;
       const auto a = ld16<T>(o + base);
       const auto b = ld16<T>(dout + base);
 #pragma unroll
@@ -96,7 +100,8 @@ __global__ __launch_bounds__(kDsinkThreads) void dsink_kernel(const float* __res
 }
 
 // dq[i] = RNE(scale * dq_accum[i]) for 8 consecutive elements per thread
-// (the main pass accumulates dS' K with dS' = dS / scale).
+// (the main pass accumulates dS' K with dS' = dS / scale).  dq and dq_accum
+// share their layout, so the cast is flat.
 template <typename T>
 __global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ src,
                                                    T* __restrict__ dst, size_t n8, float scale) {
@@ -119,14 +124,17 @@ static hipError_t preprocess_t(const Problem& p, const void* o, const void* dout
                                float* dq_accum, float* dsink, hipStream_t stream) {
   if (p.total > 0) {
     dim3 grid((p.total + 63) / 64, p.hq);
+    const int seq_len = p.bhsd ? p.max_seqlen : 0;
+    const uint32_t row = p.bhsd ? (uint32_t)p.d : (uint32_t)p.hq * p.d;  // between rows of a head
+    const uint32_t head = p.bhsd ? (uint32_t)p.max_seqlen * p.d : (uint32_t)p.d;
     if (dq_accum)
       hipLaunchKernelGGL((delta_kernel<T, D, true>), grid, dim3(256), 0, stream,
                          static_cast<const T*>(o), static_cast<const T*>(dout), delta, dq_accum,
-                         p.total, p.hq);
+                         p.total, p.hq, seq_len, row, head);
     else
       hipLaunchKernelGGL((delta_kernel<T, D, false>), grid, dim3(256), 0, stream,
                          static_cast<const T*>(o), static_cast<const T*>(dout), delta, dq_accum,
-                         p.total, p.hq);
+                         p.total, p.hq, seq_len, row, head);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -22,16 +22,16 @@ from typing import Optional
 import torch
 
 from . import (Shape, attn_bwd, attn_bwd_dkdv, attn_bwd_dq, attn_bwd_postprocess,
-               attn_bwd_preprocess, attn_fwd)
+               attn_bwd_preprocess, attn_fwd, kvshape, qshape)
 
 DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
 
 
-def make_shape(cu_lengths, hq, hkv, d, dtype, causal, window, scale) -> Shape:
+def make_shape(cu_lengths, hq, hkv, d, dtype, causal, window, scale, layout="thd") -> Shape:
     lengths = list(cu_lengths)
     return Shape.make(num_seqs=len(lengths), max_seqlen=max(1, max(lengths) if lengths else 1),
                       total_tokens=sum(lengths), hq=hq, hkv=hkv, head_dim=d, causal=causal,
-                      window=window, scale=scale, dtype=dtype)
+                      window=window, scale=scale, dtype=dtype, layout=layout)
 
 
 @dataclass
@@ -58,34 +58,43 @@ class Workspace:
     dsink: Optional[torch.Tensor]
 
 
-def to_device(x: dict, device="cuda") -> Inputs:
-    """Device tensors from a workload dict (``attn_inputs.generate``)."""
+def to_device(x: dict, device="cuda", layout="thd") -> Inputs:
+    """Device tensors from a workload dict (``attn_inputs.generate``, packed
+    [T, H, D]).  layout "bhsd" (a dense batch only) stores them as
+    [B, H, S, D] and passes no cu_seqlens."""
     dt = DTYPES[x["dtype"]]
     shape = make_shape(x["lengths"], x["hq"], x["hkv"], x["d"], dt, x["causal"], x["window"],
-                       x["scale"])
+                       x["scale"], layout)
+    lengths = [int(n) for n in x["lengths"]]
 
     def dev(a):
-        return torch.from_numpy(a).to(device=device).to(dt).contiguous()
+        t = torch.from_numpy(a).to(device=device).to(dt)
+        if layout == "bhsd":
+            if len(set(lengths)) != 1:
+                raise ValueError("the [B, H, S, D] layout needs sequences of equal length")
+            t = t.reshape(len(lengths), lengths[0], t.shape[1], t.shape[2]).transpose(1, 2)
+        return t.contiguous()
 
     sink = None if x["sink"] is None else torch.from_numpy(x["sink"]).to(device)
-    cu = torch.from_numpy(x["cu_seqlens"]).to(device=device, dtype=torch.int32)
-    return Inputs(shape, dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["do"]), cu, sink,
-                  [int(n) for n in x["lengths"]])
+    cu = None if layout == "bhsd" else \
+        torch.from_numpy(x["cu_seqlens"]).to(device=device, dtype=torch.int32)
+    return Inputs(shape, dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["do"]), cu, sink, lengths)
 
 
 def workspace(inp: Inputs) -> Workspace:
     s = inp.shape
-    T, Hq, Hkv, D = s.total_tokens, s.hq, s.hkv, s.head_dim
+    T, Hq = s.total_tokens, s.hq
     dev, dt = inp.q.device, inp.q.dtype
     f32 = torch.float32
+    qs, kvs = qshape(s), kvshape(s)
     return Workspace(
-        o=torch.empty(T, Hq, D, device=dev, dtype=dt),
+        o=torch.empty(qs, device=dev, dtype=dt),
         lse=torch.empty(Hq, T, device=dev, dtype=f32),
         delta=torch.empty(Hq, T, device=dev, dtype=f32),
-        dq_accum=torch.empty(T, Hq, D, device=dev, dtype=f32),
-        dq=torch.empty(T, Hq, D, device=dev, dtype=dt),
-        dk=torch.empty(T, Hkv, D, device=dev, dtype=dt),
-        dv=torch.empty(T, Hkv, D, device=dev, dtype=dt),
+        dq_accum=torch.empty(qs, device=dev, dtype=f32),
+        dq=torch.empty(qs, device=dev, dtype=dt),
+        dk=torch.empty(kvs, device=dev, dtype=dt),
+        dv=torch.empty(kvs, device=dev, dtype=dt),
         dsink=None if inp.sink is None else torch.empty(Hq, device=dev, dtype=f32),
     )
 

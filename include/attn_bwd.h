@@ -12,8 +12,9 @@
  *
  * Conventions shared by every call
  * --------------------------------
- *  - Tensors are packed "THD": all tokens of all sequences along one axis,
- *    heads next, head_dim innermost and contiguous.
+ *  - Tensors are packed "THD" by default (shape->layout = ATTN_LAYOUT_THD):
+ *    all tokens of all sequences along one axis, heads next, head_dim
+ *    innermost and contiguous.
  *      q, o, dout, dq      [T, Hq,  D]   storage dtype (fp16 or bf16)
  *      k, v, dk, dv        [T, Hkv, D]   storage dtype
  *      lse, delta          [Hq, T]       fp32 (lse: natural log)
@@ -21,6 +22,12 @@
  *      sink, dsink         [Hq]          fp32
  *      cu_seqlens          [num_seqs+1]  int32, sequence s spans tokens
  *                                        [cu_seqlens[s], cu_seqlens[s+1])
+ *  - With shape->layout = ATTN_LAYOUT_BHSD (the [ASC] kernels' "BHSD" layout)
+ *    the batch is dense (B = num_seqs sequences of S = max_seqlen tokens,
+ *    cu_seqlens NULL) and the 16-bit tensors and dq_accum are [B, H, S, D]
+ *    (each head's rows contiguous): q, o, dout, dq, dq_accum [B, Hq, S, D],
+ *    k, v, dk, dv [B, Hkv, S, D].  lse / delta stay [Hq, T] with token
+ *    t = b * S + s.  Results are the same as for the same data packed THD.
  *  - All pointers are DEVICE pointers owned by the caller.  The library never
  *    allocates, frees or retains them and keeps no state between calls.
  *  - Every call only enqueues work on `stream` (NULL = the default stream) and
@@ -58,7 +65,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef enum {
   ATTN_OK = 0,
@@ -69,6 +76,13 @@ typedef enum {
 } attn_status_t;
 
 typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+/* Layout of the 16-bit tensors (q, k, v, o, dout, dq, dk, dv) and of dq_accum. */
+typedef enum {
+  ATTN_LAYOUT_THD = 0, /* packed [T, H, D] (varlen via cu_seqlens, or a dense batch) */
+  ATTN_LAYOUT_BHSD = 1 /* [B, H, S, D] dense batch: B = num_seqs, S = max_seqlen,
+                          T = B * S, cu_seqlens must be NULL */
+} attn_layout_t;
 
 /* Problem description shared by every call. */
 typedef struct {
@@ -82,6 +96,7 @@ typedef struct {
   int32_t window;       /* 0: none; W > 0: sliding window (requires causal) */
   float scale;          /* score scale, typically 1/sqrt(D); finite and > 0 */
   int32_t dtype;        /* attn_dtype_t of q/k/v/o/dout/dq/dk/dv */
+  int32_t layout;       /* attn_layout_t (0 = packed THD) */
 } attn_shape_t;
 
 /*

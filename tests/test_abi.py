@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     L = ab.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert ab.attn_abi_version() == 2
+    assert ab.attn_abi_version() == 3
     assert L.attn_status_string(0) == b"ok"
     assert L.attn_status_string(1) == b"invalid argument"
 
@@ -66,6 +66,9 @@ def _fwd(shape, q=FAKE, k=FAKE, v=FAKE, cu=None, sink=None, o=FAKE, lse=FAKE):
     (dict(scale=0.0), 1),
     (dict(scale=float("nan")), 1),
     (dict(total_tokens=100), 1),  # dense batch without cu_seqlens needs T = B * N
+    (dict(layout=2), 1),
+    (dict(layout=1, total_tokens=100), 1),  # [B, H, S, D] needs T = B * S
+    (dict(layout=1, max_seqlen=1 << 26, total_tokens=1 << 27, hq=1, hkv=1), 1),  # S * D >= 2^32
 ])
 def test_shape_validation(kw, status):
     assert _fwd(_shape(**kw)) == status
@@ -106,6 +109,22 @@ def test_pointer_validation():
     assert L.attn_bwd_dq(ctypes.byref(_shape(head_dim=96)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                          None, FAKE, None) == 2
     assert L.attn_bwd_postprocess(None, FAKE, FAKE, None) == 1
+
+
+def test_bhsd_layout_rejects_cu_seqlens():
+    s = _shape(layout=1)
+    assert _fwd(s, cu=FAKE) == 1
+    assert b"cu_seqlens must be NULL" in ab.lib().attn_last_error()
+    assert _fwd(_shape(layout=1, total_tokens=0, num_seqs=1, max_seqlen=1)) == 1  # T != B * S
+
+
+def test_shape_struct_matches_the_header():
+    # attn_shape_t: eleven 4-byte fields, layout last
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct {"):text.index("} attn_shape_t;")]
+    fields = re.findall(r"^\s*(?:int32_t|float)\s+(\w+);", body, flags=re.M)
+    assert fields == [f for f, _ in ab.Shape._fields_]
+    assert ctypes.sizeof(ab.Shape) == 4 * len(fields)
 
 
 def test_empty_problem_launches_nothing():
