@@ -203,13 +203,13 @@ def _traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
-def run_gpu(x: dict, steps: int, warmup: int) -> dict:
+def run_gpu(x: dict, steps: int, warmup: int, layout: str = "thd") -> dict:
     import torch
 
     from atomics_bwd_preprocess_amd import (attn_bwd, attn_bwd_dkdv, attn_bwd_dq,
                                             attn_bwd_postprocess, attn_bwd_preprocess, path)
 
-    inp = path.to_device(x, "cuda")
+    inp = path.to_device(x, "cuda", layout=layout)
     ws = path.workspace(inp)
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
@@ -419,12 +419,15 @@ def main(argv=None) -> int:
         cases = [("mha_causal", n) for n in ai.MHA_SWEEP if n != args.n or w.name != "mha_causal"]
         cases += [(nm, None) for nm in ("varlen_gqa", "sink_window", "long_gqa")
                   if nm != w.name]
-        for nm, n in cases:
+        cases = [(nm, n, "thd") for nm, n in cases]
+        if w.name == "mha_causal":  # the same dense batch as [B, H, S, D] tensors
+            cases.append(("mha_causal", args.n, "bhsd"))
+        for nm, n, layout in cases:
             wx = ai.workload(nm, n=n) if n else ai.workload(nm)
             xx = ai.generate(wx, args.seed)
-            rr = run_gpu(xx, max(3, args.steps // 4), 2)
+            rr = run_gpu(xx, max(3, args.steps // 4), 2, layout)
             f = bwd_flops(xx)
-            key = f"{nm}_n{n}" if n else nm
+            key = (f"{nm}_n{n}" if n else nm) + ("_bhsd" if layout == "bhsd" else "")
             extra[key] = {"bwd_tflops": round(f / ((rr["pre_ms"] + rr["bwd_ms"] + rr["post_ms"])
                                                    * 1e-3) / 1e12, 2),
                           "attn_bwd_kernel_tflops": round(f / (rr["bwd_ms"] * 1e-3) / 1e12, 2),
