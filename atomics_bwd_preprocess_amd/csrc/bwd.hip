@@ -49,6 +49,11 @@
 // One workgroup barrier per pair.
 //
 // The sink needs no term here: it only enters through lse.
+//
+// Variants (template parameters): WIN for sliding windows; DQ = false drops
+// the dQ product and its atomics (the dK / dV pass of the deterministic
+// backward, paired with the query-stationary dQ pass in dq.hip); BHSD for
+// [B, H, S, D] tensors (row and head strides swapped, see row_off).
 #include <limits.h>
 
 #include "common.h"
