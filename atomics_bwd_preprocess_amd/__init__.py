@@ -23,6 +23,9 @@ __all__ = [
     "attn_bwd_postprocess",
     "attn_bwd_dkdv",
     "attn_bwd_dq",
+    "attn_bwd_split",
+    "attn_bwd_dkv_reduce",
+    "MAX_SPLIT",
     "attn_abi_version",
     "LIB_PATH",
 ]
@@ -32,6 +35,7 @@ LIB_PATH = os.path.join(_PKG, "libattn_bwd.so")
 
 ATTN_F16, ATTN_BF16 = 0, 1
 ATTN_LAYOUT_THD, ATTN_LAYOUT_BHSD = 0, 1
+MAX_SPLIT = 16  # ATTN_MAX_SPLIT
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_HIP"}
 
 
@@ -89,6 +93,8 @@ def lib() -> ctypes.CDLL:
             "attn_bwd_postprocess": [S, P, P, P],
             "attn_bwd_dkdv": [S, P, P, P, P, P, P, P, P, P, P],
             "attn_bwd_dq": [S, P, P, P, P, P, P, P, P, P],
+            "attn_bwd_split": [S, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P],
+            "attn_bwd_dkv_reduce": [S, P, ctypes.c_int32, P, P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -280,3 +286,40 @@ def attn_bwd_dq(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dq, stream=
     _check(lib().attn_bwd_dq(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                              _ptr(lse), _ptr(delta), _cu(shape, cu_seqlens), _ptr(dq),
                              _stream(stream)))
+
+
+def dkv_partial_shape(shape: Shape, nsplit: int) -> tuple:
+    """Shape of the fp32 dK / dV partial workspace of attn_bwd_split."""
+    return (int(nsplit), 2) + kvshape(shape)
+
+
+def attn_bwd_split(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dq_accum, dkv_partial,
+                   nsplit: int, stream=None) -> None:
+    """Main backward with every key block's pairs split over nsplit workgroups: dQ / scale
+    into dq_accum (atomics; None: no dQ product), fp32 dK / dV partials into dkv_partial."""
+    import torch
+
+    T, Hq, Hkv, D, dt = _dims(shape)
+    _need(q, "q", dt, qshape(shape))
+    _need(k, "k", dt, kvshape(shape))
+    _need(v, "v", dt, kvshape(shape))
+    _need(dout, "dout", dt, qshape(shape))
+    _need(lse, "lse", torch.float32, (Hq, T))
+    _need(delta, "delta", torch.float32, (Hq, T))
+    _need(dq_accum, "dq_accum", torch.float32, qshape(shape), allow_none=True)
+    _need(dkv_partial, "dkv_partial", torch.float32, dkv_partial_shape(shape, nsplit))
+    _check(lib().attn_bwd_split(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                _ptr(lse), _ptr(delta), _cu(shape, cu_seqlens), _ptr(dq_accum),
+                                _ptr(dkv_partial), int(nsplit), _stream(stream)))
+
+
+def attn_bwd_dkv_reduce(shape: Shape, dkv_partial, nsplit: int, dk, dv, stream=None) -> None:
+    """dk, dv = RNE casts of the fixed-order sums of the nsplit partial slots."""
+    import torch
+
+    T, Hq, Hkv, D, dt = _dims(shape)
+    _need(dkv_partial, "dkv_partial", torch.float32, dkv_partial_shape(shape, nsplit))
+    _need(dk, "dk", dt, kvshape(shape))
+    _need(dv, "dv", dt, kvshape(shape))
+    _check(lib().attn_bwd_dkv_reduce(ctypes.byref(shape), _ptr(dkv_partial), int(nsplit),
+                                     _ptr(dk), _ptr(dv), _stream(stream)))

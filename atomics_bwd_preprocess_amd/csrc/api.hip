@@ -203,6 +203,44 @@ attn_status_t attn_bwd_dq(const attn_shape_t* shape, const void* q, const void* 
                     "attn_bwd_dq");
 }
 
+attn_status_t attn_bwd_split(const attn_shape_t* shape, const void* q, const void* k,
+                             const void* v, const void* dout, const float* lse,
+                             const float* delta, const int32_t* cu_seqlens, float* dq_accum,
+                             float* dkv_partial, int32_t nsplit, hipStream_t stream) {
+  attn::Problem p;
+  attn_status_t st = check_shape(shape, cu_seqlens, true, p);
+  if (st != ATTN_OK) return st;
+  REQUIRE_TENSOR(q);
+  REQUIRE_TENSOR(k);
+  REQUIRE_TENSOR(v);
+  REQUIRE_TENSOR(dout);
+  REQUIRE_F32(lse);
+  REQUIRE_F32(delta);
+  if (dq_accum) REQUIRE(aligned(dq_accum, 16), "dq_accum is not 16-byte aligned");
+  REQUIRE_TENSOR(dkv_partial);
+  REQUIRE(nsplit >= 1 && nsplit <= ATTN_MAX_SPLIT, "nsplit must be in [1, %d] (got %d)",
+          ATTN_MAX_SPLIT, nsplit);
+  if (p.total == 0) return ok();
+  return hip_status(attn::launch_bwd_split(p, q, k, v, dout, lse, delta, cu_seqlens, dq_accum,
+                                           dkv_partial, nsplit, stream),
+                    "attn_bwd_split");
+}
+
+attn_status_t attn_bwd_dkv_reduce(const attn_shape_t* shape, const float* dkv_partial,
+                                  int32_t nsplit, void* dk, void* dv, hipStream_t stream) {
+  attn::Problem p;
+  attn_status_t st = check_shape(shape, nullptr, false, p);
+  if (st != ATTN_OK) return st;
+  REQUIRE_TENSOR(dkv_partial);
+  REQUIRE_TENSOR(dk);
+  REQUIRE_TENSOR(dv);
+  REQUIRE(nsplit >= 1 && nsplit <= ATTN_MAX_SPLIT, "nsplit must be in [1, %d] (got %d)",
+          ATTN_MAX_SPLIT, nsplit);
+  if (p.total == 0) return ok();
+  return hip_status(attn::launch_dkv_reduce(p, dkv_partial, nsplit, dk, dv, stream),
+                    "attn_bwd_dkv_reduce");
+}
+
 attn_status_t attn_bwd_postprocess(const attn_shape_t* shape, const float* dq_accum, void* dq,
                                    hipStream_t stream) {
   attn::Problem p;

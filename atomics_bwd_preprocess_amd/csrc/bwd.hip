@@ -53,7 +53,11 @@
 // Variants (template parameters): WIN for sliding windows; DQ = false drops
 // the dQ product and its atomics (the dK / dV pass of the deterministic
 // backward, paired with the query-stationary dQ pass in dq.hip); BHSD for
-// [B, H, S, D] tensors (row and head strides swapped, see row_off).
+// [B, H, S, D] tensors (row and head strides swapped, see row_off); SPLIT
+// divides the pair loop of every key block over nsplit workgroups, each of
+// which writes its fp32 dK / dV partial to a workspace slot of its own (no
+// atomics; a reduce pass sums the slots in a fixed order and casts), for
+// problems whose longest key block would otherwise set the critical path.
 #include <limits.h>
 
 #include "common.h"
@@ -116,6 +120,8 @@ struct BwdArgs {
   int num_seqs, max_seqlen, total, hq, hkv, window;
   bool causal;
   float scale, scale_log2;
+  float* dkv_part;  // SPLIT: fp32 partials [nsplit][2][dk-shaped]
+  int nsplit;
 };
 
 // Key-major dS tile (BM queries per row): 8-byte slot s of row r lives at
@@ -138,7 +144,8 @@ __device__ __forceinline__ int dst_off(int r, int q) {  // q: multiple of 4
 // DQ: false builds the pass without its dQ product (dK / dV only, for use
 // with the query-stationary dQ pass): no dS tile in LDS, no atomics.
 // BHSD: [B, H, S, D] tensors instead of packed [T, H, D].
-template <typename T, int D, bool WIN, bool DQ, bool BHSD>
+// SPLIT: pairs of a key block split over p.nsplit workgroups (see above).
+template <typename T, int D, bool WIN, bool DQ, bool BHSD, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   using C = Cfg<D>;
   using T8 = typename V8<T>::type;
@@ -153,9 +160,18 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   // Key-block index slowest: every (sequence, kv head) starts with its
   // largest causal workload, and the blocks of one (sequence, kv head) stay
   // a multiple of 8 apart whenever num_seqs * Hkv is (same XCD and L2).
+  // With SPLIT the part index sits between the key block and (seq, kv head).
   const int nsg = p.num_seqs * p.hkv;
-  const int jb = blockIdx.x / nsg;
-  const int rem = blockIdx.x % nsg;
+  int jb, rem, part = 0;
+  if constexpr (SPLIT) {
+    jb = blockIdx.x / (nsg * p.nsplit);
+    const int r2 = blockIdx.x % (nsg * p.nsplit);
+    part = r2 / nsg;
+    rem = r2 % nsg;
+  } else {
+    jb = blockIdx.x / nsg;
+    rem = blockIdx.x % nsg;
+  }
   const int s = rem / p.hkv, g = rem % p.hkv;
   int a, b;
   seq_bounds(p.cu, s, p.max_seqlen, p.total, a, b);
@@ -215,6 +231,13 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   if (p.window > 0) ib1 = min(ib1, (kv_last + p.window - 1) / BM + 1);
   const int nq = ib1 - ib0;
   const int npairs = G * nq;
+  // This workgroup's pairs: i_lo + [0, np), all of them or part `part` of
+  // nsplit (possibly none).  The loop counts from zero in either case.
+  int i_lo = 0, np = npairs;
+  if constexpr (SPLIT) {
+    i_lo = (int)((long long)part * npairs / p.nsplit);
+    np = (int)((long long)(part + 1) * npairs / p.nsplit) - i_lo;
+  }
   const int wk_lo = kv0 + 32 * kKT * w;
 
   // Prefetch: Q / dO of a pair go straight into LDS (buffer_load ... lds);
@@ -272,11 +295,13 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     }
   };
 
-  load_pair(0, 0);
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
-  store_pair(0);
-  if (npairs > 1) load_pair(1, 1);
-  __syncthreads();
+  if (!SPLIT || np > 0) {  // workgroup-uniform; unsplit blocks always have pairs
+    load_pair(i_lo, 0);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    store_pair(0);
+    if (np > 1) load_pair(i_lo + 1, 1);
+    __syncthreads();
+  }
 
   // dQ tiles of this wave (16x16x32 MFMA): query tile dq_qt, dim tiles dq_dt
   // and dq_dt + 1.  C layout: lane l holds dim l % 16 of rows 4 (l / 16) + r.
@@ -298,8 +323,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     }
   };
 
-  for (int i = 0; i < npairs; ++i) {
-    const int buf = i & 1;
+  for (int j = 0; j < np; ++j) {
+    const int i = i_lo + j;
+    const int buf = j & 1;
     const int h = g * G + i / nq;
     const int q0 = (ib0 + i % nq) * BM;
     const char* qs = smem + C::Q_OFF + buf * C::QT;
@@ -315,13 +341,13 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
       // Every path through the tile issues all 8 pending atomics of the
       // previous pair (the barrier's wait count relies on it).
       if constexpr (TRICKLE) {
-        if (kt == 0 && i > 0) flush(0, 2);
+        if (kt == 0 && j > 0) flush(0, 2);
       }
       const bool empty = tk_lo >= L || q0 >= L || (p.causal && tk_lo > q0 + BM - 1) ||
                          (p.window > 0 && tk_hi <= q0 - p.window);
       if (empty) {
         if constexpr (TRICKLE) {
-          if (kt == 0 && i > 0) flush(2, 4);
+          if (kt == 0 && j > 0) flush(2, 4);
         }
         // With WIN the dQ product below skips exactly the key tiles that no
         // query of the block can see, so their dS rows are never read;
@@ -393,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
         }
       }
       if constexpr (TRICKLE) {
-        if (kt == 0 && i > 0) {
+        if (kt == 0 && j > 0) {
           __builtin_amdgcn_sched_barrier(0);
           flush(2, 4);
           __builtin_amdgcn_sched_barrier(0);
@@ -453,20 +479,20 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
 
     // -- next pair's lse / Delta into the other buffer (register path); the
     //    copies for the pair after it go out before this pair's atomics.
-    if (i + 1 < npairs) store_pair(buf ^ 1);
+    if (j + 1 < np) store_pair(buf ^ 1);
     // The copies for pair i + 1 must have landed: after them this wave
     // issued the two lse / Delta register loads (unless those are copies
     // too) and, except on the first pair, the 8 atomics of pair i - 1
     // (memory operations complete in order).
     {
       constexpr int after = C::LSE_DMA ? 0 : 2;
-      if (i == 0 || !DQ)
+      if (j == 0 || !DQ)
         __builtin_amdgcn_s_waitcnt(kVmcnt0 + after);
       else
         __builtin_amdgcn_s_waitcnt(kVmcnt0 + after + 8);
     }
     __syncthreads();
-    if (i + 2 < npairs) load_pair(i + 2, buf);
+    if (j + 2 < np) load_pair(i + 2, buf);
 
     if constexpr (DQ) {
       // -- dQ partial = dS K for this wave's two 16 x 16 tiles.  Slot (g, e)
@@ -527,6 +553,26 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   if constexpr (TRICKLE) flush(0, 4);
 
   // ---- single write of dK and dV (C layout: column = dim, row = key) -------
+  if constexpr (SPLIT) {
+    // fp32 partials into slot `part` (dK already scaled); rows past the
+    // sequence end fall outside the resource and are dropped.
+    const size_t n_kv = (size_t)p.total * p.hkv * D;
+    float* slot = p.dkv_part + (size_t)part * 2 * n_kv + kv_base;
+    const rsrc_t pkr = make_rsrc(slot, nkeys * kv_row * 4);
+    const rsrc_t pvr = make_rsrc(slot + n_kv, nkeys * kv_row * 4);
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t row = 32 * kKT * w + 32 * kt + (r >> 2) * 8 + 4 * c + (r & 3);
+          const uint32_t off = (row * kv_row + 32 * t + n) * 4;
+          buf_store_f32(pkr, off, dk[kt][t][r] * p.scale);
+          buf_store_f32(pvr, off, dv[kt][t][r]);
+        }
+    return;
+  }
   const rsrc_t dkr = make_rsrc(static_cast<T*>(p.dk) + kv_base, nkeys * kv_row * 2);
   const rsrc_t dvr = make_rsrc(static_cast<T*>(p.dv) + kv_base, nkeys * kv_row * 2);
 #pragma unroll
@@ -542,29 +588,32 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
       }
 }
 
+template <typename T, int D, bool DQ, bool BHSD>
+hipError_t bwd_t2(const BwdArgs& args, unsigned blocks, hipStream_t stream) {
+  const dim3 grid(blocks), block(kThreads);
+  // The split kernel is built without the window specialisation (it is
+  // still correct for windows, whose key blocks are short anyway).
+  if (args.dkv_part)
+    hipLaunchKernelGGL((bwd_kernel<T, D, false, DQ, BHSD, true>), grid, block, 0, stream, args);
+  else if (args.window > 0)
+    hipLaunchKernelGGL((bwd_kernel<T, D, true, DQ, BHSD, false>), grid, block, 0, stream, args);
+  else
+    hipLaunchKernelGGL((bwd_kernel<T, D, false, DQ, BHSD, false>), grid, block, 0, stream, args);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool DQ>
 hipError_t bwd_t(const BwdArgs& args, int nkb, bool bhsd, hipStream_t stream) {
-  const unsigned blocks = (unsigned)nkb * args.num_seqs * args.hkv;
-  const dim3 grid(blocks), block(kThreads);
-  if (args.window > 0) {
-    if (bhsd)
-      hipLaunchKernelGGL((bwd_kernel<T, D, true, DQ, true>), grid, block, 0, stream, args);
-    else
-      hipLaunchKernelGGL((bwd_kernel<T, D, true, DQ, false>), grid, block, 0, stream, args);
-  } else {
-    if (bhsd)
-      hipLaunchKernelGGL((bwd_kernel<T, D, false, DQ, true>), grid, block, 0, stream, args);
-    else
-      hipLaunchKernelGGL((bwd_kernel<T, D, false, DQ, false>), grid, block, 0, stream, args);
-  }
-  return hipGetLastError();
+  const unsigned blocks = (unsigned)nkb * args.num_seqs * args.hkv * (unsigned)args.nsplit;
+  return bhsd ? bwd_t2<T, D, DQ, true>(args, blocks, stream)
+              : bwd_t2<T, D, DQ, false>(args, blocks, stream);
 }
 
 template <bool DQ>
 hipError_t bwd_dispatch(const Problem& p, const void* q, const void* k, const void* v,
                         const void* dout, const float* lse, const float* delta,
                         const int32_t* cu, float* dq_accum, void* dk, void* dv,
-                        hipStream_t stream) {
+                        float* dkv_part, int nsplit, hipStream_t stream) {
   BwdArgs a;
   a.q = q;
   a.k = k;
@@ -585,6 +634,8 @@ hipError_t bwd_dispatch(const Problem& p, const void* q, const void* k, const vo
   a.causal = p.causal;
   a.scale = p.scale;
   a.scale_log2 = p.scale * kLog2e;
+  a.dkv_part = dkv_part;
+  a.nsplit = nsplit;
   const int nkb = (p.max_seqlen + kBN - 1) / kBN;
   if (p.bf16)
     return p.d == 64 ? bwd_t<__bf16, 64, DQ>(a, nkb, p.bhsd, stream)
@@ -599,13 +650,24 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
                       const void* dout, const float* lse, const float* delta,
                       const int32_t* cu, float* dq_accum, void* dk, void* dv,
                       hipStream_t stream) {
-  return bwd_dispatch<true>(p, q, k, v, dout, lse, delta, cu, dq_accum, dk, dv, stream);
+  return bwd_dispatch<true>(p, q, k, v, dout, lse, delta, cu, dq_accum, dk, dv, nullptr, 1, stream);
 }
 
 hipError_t launch_bwd_dkdv(const Problem& p, const void* q, const void* k, const void* v,
                            const void* dout, const float* lse, const float* delta,
                            const int32_t* cu, void* dk, void* dv, hipStream_t stream) {
-  return bwd_dispatch<false>(p, q, k, v, dout, lse, delta, cu, nullptr, dk, dv, stream);
+  return bwd_dispatch<false>(p, q, k, v, dout, lse, delta, cu, nullptr, dk, dv, nullptr, 1, stream);
+}
+
+hipError_t launch_bwd_split(const Problem& p, const void* q, const void* k, const void* v,
+                            const void* dout, const float* lse, const float* delta,
+                            const int32_t* cu, float* dq_accum, float* dkv_part, int nsplit,
+                            hipStream_t stream) {
+  if (dq_accum)
+    return bwd_dispatch<true>(p, q, k, v, dout, lse, delta, cu, dq_accum, nullptr, nullptr,
+                              dkv_part, nsplit, stream);
+  return bwd_dispatch<false>(p, q, k, v, dout, lse, delta, cu, nullptr, nullptr, nullptr,
+                             dkv_part, nsplit, stream);
 }
 
 }  // namespace attn

@@ -121,6 +121,9 @@ __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void buf_store_b16(rsrc_t r, uint32_t off, unsigned short v) {
   __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
 }
+__device__ __forceinline__ void buf_store_f32(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+}
 __device__ __forceinline__ void buf_atomic_add(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, off, 0, 0);
 }

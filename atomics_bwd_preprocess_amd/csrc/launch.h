@@ -53,6 +53,17 @@ hipError_t launch_bwd_dq(const Problem& p, const void* q, const void* k, const v
                          const void* dout, const float* lse, const float* delta,
                          const int32_t* cu, void* dq, hipStream_t stream);
 
+// Main pass with the pairs of every key block split over nsplit workgroups;
+// fp32 dK / dV partials into dkv_part (no dQ product when dq_accum is NULL).
+hipError_t launch_bwd_split(const Problem& p, const void* q, const void* k, const void* v,
+                            const void* dout, const float* lse, const float* delta,
+                            const int32_t* cu, float* dq_accum, float* dkv_part, int nsplit,
+                            hipStream_t stream);
+
+// Sum of the nsplit partial slots, cast to dk / dv.
+hipError_t launch_dkv_reduce(const Problem& p, const float* dkv_part, int nsplit, void* dk,
+                             void* dv, hipStream_t stream);
+
 hipError_t launch_postprocess(const Problem& p, const float* dq_accum, void* dq,
                               hipStream_t stream);
 

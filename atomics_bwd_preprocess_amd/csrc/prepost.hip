@@ -118,6 +118,33 @@ __global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ src
   st16<T>(dst + 8 * i, r);
 }
 
+// dk[i] = RNE(sum_p part[p][0][i]), dv[i] = RNE(sum_p part[p][1][i]) over the
+// nsplit fp32 partial slots in a fixed order (p ascending), 8 consecutive
+// elements per thread; dk, dv and the slots share their layout.
+template <typename T>
+__global__ __launch_bounds__(256) void dkv_reduce_kernel(const float* __restrict__ part, int nsplit,
+                                                         size_t n_kv, T* __restrict__ dk,
+                                                         T* __restrict__ dv) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_kv / 8) return;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nsplit; ++s) {
+      const float* src = part + ((size_t)s * 2 + which) * n_kv + 8 * i;
+      a += *reinterpret_cast<const f32x4*>(src);
+      b += *reinterpret_cast<const f32x4*>(src + 4);
+    }
+    typename V8<T>::type r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      r[k] = to16<T>(a[k]);
+      r[k + 4] = to16<T>(b[k]);
+    }
+    st16<T>((which ? dv : dk) + 8 * i, r);
+  }
+}
+
 template <typename T, int D>
 static hipError_t preprocess_t(const Problem& p, const void* o, const void* dout,
                                const float* lse, const float* sink, float* delta,
@@ -164,6 +191,19 @@ hipError_t launch_postprocess(const Problem& p, const float* dq_accum, void* dq,
   else
     hipLaunchKernelGGL(cast_kernel<_Float16>, grid, dim3(256), 0, stream, dq_accum,
                        static_cast<_Float16*>(dq), n8, p.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_dkv_reduce(const Problem& p, const float* dkv_part, int nsplit, void* dk,
+                             void* dv, hipStream_t stream) {
+  const size_t n_kv = (size_t)p.total * p.hkv * p.d;
+  const dim3 grid((unsigned)((n_kv / 8 + 255) / 256));
+  if (p.bf16)
+    hipLaunchKernelGGL(dkv_reduce_kernel<__bf16>, grid, dim3(256), 0, stream, dkv_part, nsplit,
+                       n_kv, static_cast<__bf16*>(dk), static_cast<__bf16*>(dv));
+  else
+    hipLaunchKernelGGL(dkv_reduce_kernel<_Float16>, grid, dim3(256), 0, stream, dkv_part, nsplit,
+                       n_kv, static_cast<_Float16*>(dk), static_cast<_Float16*>(dv));
   return hipGetLastError();
 }
 

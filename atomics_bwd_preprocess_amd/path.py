@@ -21,8 +21,9 @@ from typing import Optional
 
 import torch
 
-from . import (Shape, attn_bwd, attn_bwd_dkdv, attn_bwd_dq, attn_bwd_postprocess,
-               attn_bwd_preprocess, attn_fwd, kvshape, qshape)
+from . import (MAX_SPLIT, Shape, attn_bwd, attn_bwd_dkdv, attn_bwd_dkv_reduce, attn_bwd_dq,
+               attn_bwd_postprocess, attn_bwd_preprocess, attn_bwd_split, attn_fwd,
+               dkv_partial_shape, kvshape, qshape)
 
 DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -56,6 +57,7 @@ class Workspace:
     dk: torch.Tensor
     dv: torch.Tensor
     dsink: Optional[torch.Tensor]
+    dkv_part: Optional[torch.Tensor] = None  # fp32 partials of a split backward
 
 
 def to_device(x: dict, device="cuda", layout="thd") -> Inputs:
@@ -136,34 +138,105 @@ def select_mode(shape: Shape, lengths=None) -> str:
     return "deterministic" if 0 < shape.window <= 1024 else "atomic"
 
 
+# Workgroup geometry of the key/value-stationary pass (bwd.hip): 256 keys per
+# workgroup, query blocks of 64 rows (D = 64) or 32 rows (D = 128), one
+# workgroup per CU at a time on the 256 CUs.
+_BN, _CUS = 256, 256
+
+
+def _bm(shape: Shape) -> int:
+    return 32 if shape.head_dim == 128 else 64
+
+
+def pairs_per_key_block(shape: Shape, lengths=None) -> list:
+    """(query head, query block) pairs of every key-block workgroup of one kv
+    head (the main pass's loop lengths), from the host lengths."""
+    lens = list(lengths) if lengths is not None else [shape.max_seqlen] * shape.num_seqs
+    bm, G, W = _bm(shape), shape.hq // shape.hkv, shape.window
+    out = []
+    for n in lens:
+        for kv0 in range(0, n, _BN):
+            ib0 = kv0 // bm if shape.causal else 0
+            ib1 = -(-n // bm)
+            if W > 0:
+                ib1 = min(ib1, (min(n, kv0 + _BN) - 1 + W - 1) // bm + 1)
+            out.append(G * (ib1 - ib0))
+    return out
+
+
+def select_splits(shape: Shape, lengths=None) -> int:
+    """How many workgroups to split each key block's pair loop over.  Only
+    when all key-block workgroups run in one round on the CUs (then the
+    longest one is the kernel's time) and it holds clearly more pairs than
+    the mean: split so that parts of the longest match the mean.  With more
+    workgroups than CUs the longest-first order already balances them, and
+    the partial sums only add traffic (measured on MI355X: 4 x 2k D=64 MHA
+    0.114 -> 0.107 ms and one 8k D=128 GQA sequence 5.82 -> 3.69 ms with two
+    parts; the varlen batch, 464 workgroups, 1.62 -> 1.65 ms).  Never for
+    windows (short key blocks; the split kernel has no window
+    specialisation)."""
+    if shape.window > 0:
+        return 1
+    pairs = pairs_per_key_block(shape, lengths)
+    if not pairs or len(pairs) * shape.hkv > _CUS:
+        return 1
+    mean = sum(pairs) / len(pairs)
+    longest = max(pairs)
+    if longest <= 1.25 * mean:
+        return 1
+    return int(min(MAX_SPLIT, -(-longest // max(mean, 1.0))))
+
+
+def _split_workspace(inp: Inputs, ws: Workspace, nsplit: int) -> torch.Tensor:
+    want = dkv_partial_shape(inp.shape, nsplit)
+    if ws.dkv_part is None or tuple(ws.dkv_part.shape) != want:
+        ws.dkv_part = torch.empty(want, device=inp.q.device, dtype=torch.float32)
+    return ws.dkv_part
+
+
 def forward(inp: Inputs, ws: Workspace, stream=None) -> None:
     attn_fwd(inp.shape, inp.q, inp.k, inp.v, inp.cu, inp.sink, ws.o, ws.lse, stream)
 
 
 def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
-             mode: str = "atomic") -> str:
+             mode: str = "atomic", kv_splits=1) -> str:
     """Preprocess -> main backward -> postprocess; O and lse default to ws.o / ws.lse.
     mode "deterministic": dK/dV pass + query-stationary dQ pass, no atomics
-    (ws.dq_accum unused); "auto": select_mode.  Returns the mode that ran."""
+    (ws.dq_accum unused); "auto": select_mode.  kv_splits > 1 (or "auto":
+    select_splits) splits every key block's pairs over that many workgroups,
+    whose fp32 dK / dV partials are then summed in a fixed order
+    (attn_bwd_split + attn_bwd_dkv_reduce; the partials live in ws.dkv_part,
+    allocated on first use).  Returns the mode that ran."""
     if mode == "auto":
         mode = select_mode(inp.shape, inp.lengths)
     if mode not in ("atomic", "deterministic"):
         raise ValueError(f"unknown backward mode {mode!r}")
+    if kv_splits == "auto":
+        kv_splits = select_splits(inp.shape, inp.lengths)
+    kv_splits = int(kv_splits)
+    if not 1 <= kv_splits <= MAX_SPLIT:
+        raise ValueError(f"kv_splits must be in [1, {MAX_SPLIT}] (got {kv_splits})")
     o = ws.o if o is None else o
     lse = ws.lse if lse is None else lse
-    if mode == "deterministic":
-        attn_bwd_preprocess(inp.shape, o, inp.do, lse, inp.cu, inp.sink, ws.delta, None,
-                            ws.dsink, stream)
+    det = mode == "deterministic"
+    attn_bwd_preprocess(inp.shape, o, inp.do, lse, inp.cu, inp.sink, ws.delta,
+                        None if det else ws.dq_accum, ws.dsink, stream)
+    if kv_splits > 1:
+        part = _split_workspace(inp, ws, kv_splits)
+        attn_bwd_split(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu,
+                       None if det else ws.dq_accum, part, kv_splits, stream)
+        attn_bwd_dkv_reduce(inp.shape, part, kv_splits, ws.dk, ws.dv, stream)
+    elif det:
         attn_bwd_dkdv(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dk,
                       ws.dv, stream)
+    else:
+        attn_bwd(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dq_accum,
+                 ws.dk, ws.dv, stream)
+    if det:
         attn_bwd_dq(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dq,
                     stream)
-        return mode
-    attn_bwd_preprocess(inp.shape, o, inp.do, lse, inp.cu, inp.sink, ws.delta, ws.dq_accum,
-                        ws.dsink, stream)
-    attn_bwd(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dq_accum, ws.dk,
-             ws.dv, stream)
-    attn_bwd_postprocess(inp.shape, ws.dq_accum, ws.dq, stream)
+    else:
+        attn_bwd_postprocess(inp.shape, ws.dq_accum, ws.dq, stream)
     return mode
 
 

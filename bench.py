@@ -10,7 +10,8 @@ of the three backward launches.  The forward runs in every step (it produces
 O and lse) and is reported separately.  The deterministic backward
 (attn_bwd_preprocess without the accumulator -> attn_bwd_dkdv -> attn_bwd_dq,
 no atomics) is timed on the same inputs and reported under "deterministic",
-with the orientation path.select_mode picks for the shape.
+with the orientation path.select_mode picks for the shape, and the backward
+as path.backward(mode="auto", kv_splits="auto") runs it under "auto".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--n N] [--seed S] [--no-cpu-baseline] [--no-extra]
@@ -256,7 +257,18 @@ def run_gpu(x: dict, steps: int, warmup: int, layout: str = "thd") -> dict:
     torch.cuda.synchronize()
     dm = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(3)] for e in ev]).mean(axis=0)
     out.update(det_pre_ms=float(dm[0]), dkdv_ms=float(dm[1]), dq_ms=float(dm[2]),
-               auto_mode=path.select_mode(inp.shape, inp.lengths))
+               auto_mode=path.select_mode(inp.shape, inp.lengths),
+               auto_splits=path.select_splits(inp.shape, inp.lengths))
+    # The whole backward as path.backward(mode="auto", kv_splits="auto") runs it.
+    for _ in range(2):
+        path.backward(inp, ws, mode="auto", kv_splits="auto")
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        path.backward(inp, ws, mode="auto", kv_splits="auto")
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    out["auto_ms"] = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     del ws, inp
     torch.cuda.empty_cache()
     return out
@@ -276,6 +288,13 @@ def deterministic_entry(x: dict, r: dict) -> dict:
             "attn_bwd_dq_tflops": round(0.6 * f / (r["dq_ms"] * 1e-3) / 1e12, 2),
             "vs_atomic_path": round((r["pre_ms"] + r["bwd_ms"] + r["post_ms"]) / total, 4),
             "auto_mode": r["auto_mode"]}
+
+
+def auto_entry(x: dict, r: dict) -> dict:
+    """The backward as path.backward(mode="auto", kv_splits="auto") runs it."""
+    return {"mode": r["auto_mode"], "kv_splits": r["auto_splits"],
+            "bwd_ms": round(r["auto_ms"], 4),
+            "bwd_tflops": round(bwd_flops(x) / (r["auto_ms"] * 1e-3) / 1e12, 2)}
 
 
 def cpu_baseline(x: dict, min_run_s: float = 4.0) -> dict:
@@ -407,6 +426,7 @@ def main(argv=None) -> int:
                             "their device-wide rate, not the MFMA peak, bounds this kernel"},
         "wall_ms_per_step": round(r["wall_ms_per_step"], 4),
         "deterministic": deterministic_entry(x, r),
+        "auto": auto_entry(x, r),
         "device": device_info(),
     }
     base = PAGES_BASELINE.get((w.name, args.n if w.name == "mha_causal" else None))
@@ -437,6 +457,7 @@ def main(argv=None) -> int:
                           "fwd_tflops": round(fwd_flops(xx) / (rr["fwd_ms"] * 1e-3) / 1e12, 2),
                           "attn_fwd_ms": round(rr["fwd_ms"], 4)}
             extra[key]["deterministic"] = deterministic_entry(xx, rr)
+            extra[key]["auto"] = auto_entry(xx, rr)
             if xx["window"] > 0:
                 extra[key]["attn_bwd_kernel_tflops_nominal_formula"] = round(
                     bwd_flops_nominal(xx) / (rr["bwd_ms"] * 1e-3) / 1e12, 2)

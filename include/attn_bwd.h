@@ -65,7 +65,8 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
+#define ATTN_MAX_SPLIT 16 /* largest nsplit of attn_bwd_split */
 
 typedef enum {
   ATTN_OK = 0,
@@ -171,6 +172,30 @@ attn_status_t attn_bwd_dkdv(const attn_shape_t* shape, const void* q, const void
 attn_status_t attn_bwd_dq(const attn_shape_t* shape, const void* q, const void* k, const void* v,
                           const void* dout, const float* lse, const float* delta,
                           const int32_t* cu_seqlens, void* dq, hipStream_t stream);
+
+/*
+ * Main backward pass (as attn_bwd, or as attn_bwd_dkdv when dq_accum is NULL)
+ * with the query loop of every key block split over `nsplit` workgroups
+ * (1..ATTN_MAX_SPLIT), for problems whose longest key block sets the
+ * critical path (ragged varlen batches).  Part p of a key block covers an
+ * equal share of its (query head, query block) pairs and WRITES its dK / dV
+ * partial, summed in fp32 registers over that share, into slot p of
+ * dkv_partial: fp32 [nsplit][2][dk-shaped] (slot p holds dK * scale, then
+ * dV, each in the layout of dk).  Every row of every slot is written once,
+ * so no zeroing is needed.  dQ is accumulated into dq_accum exactly as in
+ * attn_bwd.  attn_bwd_dkv_reduce then forms dk and dv.
+ */
+attn_status_t attn_bwd_split(const attn_shape_t* shape, const void* q, const void* k,
+                             const void* v, const void* dout, const float* lse,
+                             const float* delta, const int32_t* cu_seqlens, float* dq_accum,
+                             float* dkv_partial, int32_t nsplit, hipStream_t stream);
+
+/*
+ * dk = RNE(sum_p dkv_partial[p][0]), dv = RNE(sum_p dkv_partial[p][1]), the
+ * sum taken in fp32 over p = 0 .. nsplit-1 in that order (deterministic).
+ */
+attn_status_t attn_bwd_dkv_reduce(const attn_shape_t* shape, const float* dkv_partial,
+                                  int32_t nsplit, void* dk, void* dv, hipStream_t stream);
 
 /*
  * Backward postprocess ([ASC] postprocess kernel casting the fp32 gradient

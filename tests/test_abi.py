@@ -27,6 +27,7 @@ def _declared():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["attn_fwd", "attn_bwd_preprocess", "attn_bwd",
                                   "attn_bwd_postprocess", "attn_bwd_dkdv", "attn_bwd_dq",
+                                  "attn_bwd_split", "attn_bwd_dkv_reduce",
                                   "attn_status_string", "attn_last_error",
                                   "attn_abi_version"])
 
@@ -35,7 +36,8 @@ def test_library_exports_every_declared_symbol():
     L = ab.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert ab.attn_abi_version() == 3
+    assert ab.attn_abi_version() == 4
+    assert ab.MAX_SPLIT == int(re.search(r"#define ATTN_MAX_SPLIT (\d+)", open(HEADER).read()).group(1))
     assert L.attn_status_string(0) == b"ok"
     assert L.attn_status_string(1) == b"invalid argument"
 
@@ -109,6 +111,27 @@ def test_pointer_validation():
     assert L.attn_bwd_dq(ctypes.byref(_shape(head_dim=96)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                          None, FAKE, None) == 2
     assert L.attn_bwd_postprocess(None, FAKE, FAKE, None) == 1
+
+
+def test_split_validation():
+    s = _shape()
+    L = ab.lib()
+
+    def split(nsplit, part=FAKE, dq=FAKE):
+        return L.attn_bwd_split(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, dq,
+                                part, nsplit, None)
+
+    assert split(0) == 1 and b"nsplit" in L.attn_last_error()
+    assert split(17) == 1
+    assert split(2, part=None) == 1 and b"dkv_partial is NULL" in L.attn_last_error()
+    assert split(2, dq=FAKE + 4) == 1 and b"dq_accum" in L.attn_last_error()
+    assert L.attn_bwd_dkv_reduce(ctypes.byref(s), FAKE, 0, FAKE, FAKE, None) == 1
+    assert L.attn_bwd_dkv_reduce(ctypes.byref(s), FAKE, 2, FAKE, None, None) == 1
+    # a valid empty problem launches nothing
+    e = _shape(total_tokens=0)
+    assert L.attn_bwd_split(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                            FAKE, 2, None) == 0
+    assert L.attn_bwd_dkv_reduce(ctypes.byref(e), FAKE, 2, FAKE, FAKE, None) == 0
 
 
 def test_bhsd_layout_rejects_cu_seqlens():

@@ -39,3 +39,5 @@ def test_bench_line_contract(capsys):
     assert d["bwd_ms"] == pytest.approx(d["attn_bwd_preprocess_ms"] + d["attn_bwd_dkdv_ms"]
                                         + d["attn_bwd_dq_ms"], abs=2e-4)
     assert d["bwd_tflops"] > 0 and d["attn_bwd_dq_tflops"] > 0
+    au = line["auto"]
+    assert au["mode"] == "deterministic" and au["kv_splits"] == 1 and au["bwd_tflops"] > 0

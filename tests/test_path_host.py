@@ -59,3 +59,61 @@ def test_unknown_mode_is_rejected_before_any_launch():
     inp = path.Inputs(_shape([4]), None, None, None, None, None, None, [4])
     with pytest.raises(ValueError):
         path.backward(inp, None, mode="fast")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 37), (True, 300)])
+def test_pairs_per_key_block_follow_the_schedule(d, causal, window):
+    from test_tile_schedule import q_range
+
+    lengths = [1, 31, 257, 700, 256]
+    s = path.make_shape(lengths, 8, 2, d, "f16", causal, window, 0.1)
+    bm = 32 if d == 128 else 64
+    want = []
+    for n in lengths:
+        for kv0 in range(0, n, 256):
+            ib0, ib1 = q_range(n, kv0, bm, causal, window)
+            want.append(4 * (ib1 - ib0))
+    assert path.pairs_per_key_block(s, lengths) == want
+
+
+@pytest.mark.parametrize("name,kw,split", [
+    ("mha_causal", dict(n=32768), False),
+    ("mha_causal", dict(n=4096), False),   # 512 workgroups: balanced by the order
+    ("mha_causal", dict(n=2048), True),    # 256 workgroups, longest 2x the mean
+    ("long_gqa", {}, False),
+    ("long_gqa", dict(seqlens=(8192,)), True),
+    ("sink_window", {}, False),   # windows are never split
+    ("varlen_gqa", {}, False),    # 464 workgroups
+])
+def test_select_splits(name, kw, split):
+    w = ai.workload(name, **{k: v for k, v in kw.items() if k == "n"})
+    if "seqlens" in kw:
+        w = w.with_(seqlens=kw["seqlens"])
+    if w.draw_lengths is not None:
+        nseq, lo, hi = w.draw_lengths
+        lengths = [int(x) for x in np.random.default_rng(0).integers(lo, hi + 1, nseq)]
+    else:
+        lengths = list(w.seqlens)
+    s = path.make_shape(lengths, w.hq, w.hkv, w.d, w.dtype, w.causal, w.window, 0.1)
+    n = path.select_splits(s, lengths)
+    assert (n > 1) == split and 1 <= n <= 16
+
+
+def test_split_parts_tile_the_pairs():
+    # part p of nsplit covers pairs [p n / nsplit, (p + 1) n / nsplit)
+    for npairs in range(1, 70):
+        for nsplit in range(1, 17):
+            covered = []
+            for p in range(nsplit):
+                lo, hi = p * npairs // nsplit, (p + 1) * npairs // nsplit
+                covered += list(range(lo, hi))
+            assert covered == list(range(npairs))
+
+
+def test_bad_split_count_is_rejected_before_any_launch():
+    inp = path.Inputs(_shape([4]), None, None, None, None, None, None, [4])
+    with pytest.raises(ValueError):
+        path.backward(inp, None, kv_splits=0)
+    with pytest.raises(ValueError):
+        path.backward(inp, None, kv_splits=17)
