@@ -61,8 +61,11 @@ struct DqArgs {
   float scale, scale_log2;
 };
 
-// BHSD: [B, H, S, D] tensors instead of packed [T, H, D].
-template <typename T, int D, bool BHSD>
+// BHSD: [B, H, S, D] tensors instead of packed [T, H, D].  WIN: sliding
+// windows, where a wave also skips the 32-key halves of a block that none of
+// its rows can see (measured 8 % faster at W = 128, 2 % slower on long
+// causal problems, hence only here).
+template <typename T, int D, bool BHSD, bool WIN>
 __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(DqArgs p) {
   using C = DqCfg<D>;
   using T8 = typename V8<T>::type;
@@ -170,10 +173,17 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(DqArgs p) {
       const char* kt = smem + stage * C::STAGE;
       const char* vt = kt + C::TILE;
       const int kb_last = kb + kDqBN - 1;
-      const bool full = (kb_last < L) && (!p.causal || kb_last <= wq_lo) &&
-                        (p.window <= 0 || kb > wq_hi - p.window);
+      bool full = (kb_last < L) && (!p.causal || kb_last <= wq_lo) &&
+                  (p.window <= 0 || kb > wq_hi - p.window);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
+        if constexpr (WIN) {
+          // Keys [h_lo, h_lo + 32): skipped when hidden from every row of
+          // the wave, masked only when hidden from some.
+          const int h_lo = kb + 32 * mt, h_hi = h_lo + 31;
+          if (h_lo >= L || (p.causal && h_lo > wq_hi) || h_hi <= wq_lo - p.window) continue;
+          full = (h_hi < L) && (!p.causal || h_hi <= wq_lo) && h_lo > wq_hi - p.window;
+        }
         // S^T and dP^T for keys [kb + 32 mt, +32) against this wave's queries.
         f32x16 st = f32x16{}, dpt = f32x16{};
 #pragma unroll
@@ -239,10 +249,18 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(DqArgs p) {
 template <typename T, int D>
 hipError_t dq_t(const DqArgs& args, bool bhsd, hipStream_t stream) {
   const unsigned blocks = (unsigned)args.nqb * args.num_seqs * args.hq;
-  if (bhsd)
-    hipLaunchKernelGGL((dq_kernel<T, D, true>), dim3(blocks), dim3(kDqThreads), 0, stream, args);
-  else
-    hipLaunchKernelGGL((dq_kernel<T, D, false>), dim3(blocks), dim3(kDqThreads), 0, stream, args);
+  const dim3 grid(blocks), block(kDqThreads);
+  if (args.window > 0) {
+    if (bhsd)
+      hipLaunchKernelGGL((dq_kernel<T, D, true, true>), grid, block, 0, stream, args);
+    else
+      hipLaunchKernelGGL((dq_kernel<T, D, false, true>), grid, block, 0, stream, args);
+  } else {
+    if (bhsd)
+      hipLaunchKernelGGL((dq_kernel<T, D, true, false>), grid, block, 0, stream, args);
+    else
+      hipLaunchKernelGGL((dq_kernel<T, D, false, false>), grid, block, 0, stream, args);
+  }
   return hipGetLastError();
 }
 

@@ -78,8 +78,10 @@ struct FwdArgs {
   float scale_log2;
 };
 
-// BHSD: [B, H, S, D] tensors instead of packed [T, H, D].
-template <typename T, int D, bool BHSD>
+// BHSD: [B, H, S, D] tensors instead of packed [T, H, D].  WIN: sliding
+// windows, where a wave also skips the products of the 32-key halves of a
+// block that none of its rows can see (their scores are -inf, their P zero).
+template <typename T, int D, bool BHSD, bool WIN>
 __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
   using C = FwdCfg<D>;
   using T8 = typename V8<T>::type;
@@ -193,11 +195,28 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
 
       // S^T for keys [kb, kb + 64) (two 32-row tiles) against this wave's queries.
       f32x16 st[2] = {f32x16{}, f32x16{}};
+      bool hvis[2] = {true, true};  // WIN: some row of the wave sees the half
+      if constexpr (WIN) {
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
+        for (int mt = 0; mt < 2; ++mt) {
+          const int h_lo = kb + 32 * mt, h_hi = h_lo + 31;
+          hvis[mt] = !(h_lo >= L || (p.causal && h_lo > wq_hi) || h_hi <= wq_lo - p.window);
+          if (hvis[mt]) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          st[mt] = mfma32(lds16<T>(kt, rm_off<D>(32 * mt + n, 16 * ks + 8 * c)), qreg[ks], st[mt]);
+            for (int ks = 0; ks < D / 16; ++ks)
+              st[mt] = mfma32(lds16<T>(kt, rm_off<D>(32 * mt + n, 16 * ks + 8 * c)), qreg[ks], st[mt]);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[mt][r] = -INFINITY;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            st[mt] = mfma32(lds16<T>(kt, rm_off<D>(32 * mt + n, 16 * ks + 8 * c)), qreg[ks], st[mt]);
+      }
 
       // Hidden keys -> -inf, only on blocks not fully visible to every row of
       // the wave.  The empty asm keeps this a real branch.
@@ -246,6 +265,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
       float lsum = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < kFwdBN / 16; ++ks) {
+        if (WIN && !hvis[ks >> 1]) continue;  // P = 0 there
         const T8 pb = pack8<T>(st[ks >> 1], 8 * (ks & 1));
         lsum = sum8(pb, lsum);
         const int row = 16 * ks + 4 * c + (l16 >> 2);
@@ -285,10 +305,18 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
 template <typename T, int D>
 hipError_t fwd_t(const FwdArgs& args, bool bhsd, hipStream_t stream) {
   const unsigned blocks = (unsigned)args.nqb * args.num_seqs * args.hq;
-  if (bhsd)
-    hipLaunchKernelGGL((fwd_kernel<T, D, true>), dim3(blocks), dim3(kFwdThreads), 0, stream, args);
-  else
-    hipLaunchKernelGGL((fwd_kernel<T, D, false>), dim3(blocks), dim3(kFwdThreads), 0, stream, args);
+  const dim3 grid(blocks), block(kFwdThreads);
+  if (args.window > 0) {
+    if (bhsd)
+      hipLaunchKernelGGL((fwd_kernel<T, D, true, true>), grid, block, 0, stream, args);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, D, false, true>), grid, block, 0, stream, args);
+  } else {
+    if (bhsd)
+      hipLaunchKernelGGL((fwd_kernel<T, D, true, false>), grid, block, 0, stream, args);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, D, false, false>), grid, block, 0, stream, args);
+  }
   return hipGetLastError();
 }
 
