@@ -52,38 +52,16 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // Round-to-nearest-even conversion of fp32 to the 16-bit storage type.
 template <typename T> __device__ __forceinline__ T to16(float x) { return static_cast<T>(x); }
 
-template <typename T> __device__ __forceinline__ typename V8<T>::type zero8() {
-  typename V8<T>::type z;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) z[i] = static_cast<T>(0.0f);
-  return z;
-}
-
-// 16-byte and 8-byte raw moves (global or LDS, by address space inference).
+// 16-byte loads / stores and 8-byte stores (global or LDS, by address space
+// inference).
 template <typename T> __device__ __forceinline__ typename V8<T>::type ld16(const T* p) {
   return __builtin_bit_cast(typename V8<T>::type, *reinterpret_cast<const u32x4*>(p));
 }
 template <typename T> __device__ __forceinline__ void st16(T* p, typename V8<T>::type v) {
   *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, v);
 }
-template <typename T> __device__ __forceinline__ typename V8<T>::half_type ld8(const T* p) {
-  return __builtin_bit_cast(typename V8<T>::half_type, *reinterpret_cast<const u32x2*>(p));
-}
 template <typename T> __device__ __forceinline__ void st8(T* p, typename V8<T>::half_type v) {
   *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v);
-}
-
-// Concatenate two 4-element halves into one 8-element MFMA operand.
-template <typename T>
-__device__ __forceinline__ typename V8<T>::type cat8(typename V8<T>::half_type lo,
-                                                     typename V8<T>::half_type hi) {
-  typename V8<T>::type r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = lo[i];
-    r[i + 4] = hi[i];
-  }
-  return r;
 }
 
 // Pack registers [base, base + 8) of an MFMA C tile into an operand.
