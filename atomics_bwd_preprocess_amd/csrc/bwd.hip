@@ -122,7 +122,53 @@ struct BwdArgs {
   float scale, scale_log2;
   float* dkv_part;  // SPLIT: fp32 partials [nsplit][2][dk-shaped]
   int nsplit;
+  int lpt;  // rank the (sequence, key block) items longest first (ragged batches)
 };
+
+// Longest-first order for ragged batches.  Key-block index slowest is
+// longest first only when every sequence has the same length; otherwise a
+// long sequence's later key blocks (still many query blocks) would start
+// after every short sequence's first one and form the tail.  Every
+// workgroup ranks the num_seqs * nkb (sequence, key block) items by their
+// number of query blocks under the masks (ties: lower item first; empty
+// items last) and takes the item of rank r.  All threads take part; it uses
+// the start of LDS and ends with a barrier.  At most kMaxLpt items (one per
+// thread, then a scan of LDS broadcasts).
+constexpr int kMaxLpt = kThreads;
+template <int BM>
+__device__ int lpt_item(const BwdArgs& p, int nkb, int r, char* smem) {
+  int* work = reinterpret_cast<int*>(smem);
+  int* found = work + kMaxLpt;
+  const int n = p.num_seqs * nkb, i = threadIdx.x;
+  int wi = -1;
+  if (i < n) {
+    const int s = i / nkb, kv0 = (i % nkb) * kBN;
+    int a, b;
+    seq_bounds(p.cu, s, p.max_seqlen, p.total, a, b);
+    const int L = b - a;
+    wi = 0;
+    if (kv0 < L) {
+      const int ib0 = p.causal ? kv0 / BM : 0;
+      int ib1 = (L + BM - 1) / BM;
+      if (p.window > 0) ib1 = min(ib1, (min(L, kv0 + kBN) - 1 + p.window - 1) / BM + 1);
+      wi = ib1 - ib0;
+    }
+    work[i] = wi;
+  }
+  __syncthreads();
+  if (i < n) {
+    int rank = 0;
+    for (int k = 0; k < n; ++k) {
+      const int wk = work[k];
+      rank += (wk > wi) | ((wk == wi) & (k < i));
+    }
+    if (rank == r) found[0] = i;
+  }
+  __syncthreads();
+  const int item = found[0];
+  __syncthreads();
+  return item;
+}
 
 // Key-major dS tile (BM queries per row): 8-byte slot s of row r lives at
 // slot s ^ slot_swz(r).  The 8-byte stores resolve 16 lanes (16 consecutive
@@ -161,18 +207,33 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
   // largest causal workload, and the blocks of one (sequence, kv head) stay
   // a multiple of 8 apart whenever num_seqs * Hkv is (same XCD and L2).
   // With SPLIT the part index sits between the key block and (seq, kv head).
+  // Ragged batches rank their (sequence, key block) items instead (lpt_item);
+  // the kv head stays fastest, so with Hkv a multiple of 8 kv head g runs on
+  // XCD g either way.
   const int nsg = p.num_seqs * p.hkv;
-  int jb, rem, part = 0;
-  if constexpr (SPLIT) {
-    jb = blockIdx.x / (nsg * p.nsplit);
-    const int r2 = blockIdx.x % (nsg * p.nsplit);
-    part = r2 / nsg;
-    rem = r2 % nsg;
+  int jb, s, g, part = 0;
+  if (p.lpt) {
+    const int nkb = (p.max_seqlen + kBN - 1) / kBN;
+    const int r = blockIdx.x / (p.hkv * (SPLIT ? p.nsplit : 1));
+    if constexpr (SPLIT) part = (blockIdx.x / p.hkv) % p.nsplit;
+    g = blockIdx.x % p.hkv;
+    const int item = uni(lpt_item<BM>(p, nkb, r, smem));
+    s = item / nkb;
+    jb = item % nkb;
   } else {
-    jb = blockIdx.x / nsg;
-    rem = blockIdx.x % nsg;
+    int rem;
+    if constexpr (SPLIT) {
+      jb = blockIdx.x / (nsg * p.nsplit);
+      const int r2 = blockIdx.x % (nsg * p.nsplit);
+      part = r2 / nsg;
+      rem = r2 % nsg;
+    } else {
+      jb = blockIdx.x / nsg;
+      rem = blockIdx.x % nsg;
+    }
+    s = rem / p.hkv;
+    g = rem % p.hkv;
   }
-  const int s = rem / p.hkv, g = rem % p.hkv;
   int a, b;
   seq_bounds(p.cu, s, p.max_seqlen, p.total, a, b);
   const int L = b - a;
@@ -637,6 +698,9 @@ hipError_t bwd_dispatch(const Problem& p, const void* q, const void* k, const vo
   a.dkv_part = dkv_part;
   a.nsplit = nsplit;
   const int nkb = (p.max_seqlen + kBN - 1) / kBN;
+  // Packed sequences of unknown (device-side) lengths are ranked in the
+  // kernel; a dense batch's formula order is already longest first.
+  a.lpt = (cu != nullptr && p.num_seqs > 1 && (long long)p.num_seqs * nkb <= kMaxLpt) ? 1 : 0;
   if (p.bf16)
     return p.d == 64 ? bwd_t<__bf16, 64, DQ>(a, nkb, p.bhsd, stream)
                      : bwd_t<__bf16, 128, DQ>(a, nkb, p.bhsd, stream);

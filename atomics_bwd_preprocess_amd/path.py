@@ -165,26 +165,25 @@ def pairs_per_key_block(shape: Shape, lengths=None) -> list:
 
 
 def select_splits(shape: Shape, lengths=None) -> int:
-    """How many workgroups to split each key block's pair loop over.  Only
-    when all key-block workgroups run in one round on the CUs (then the
-    longest one is the kernel's time) and it holds clearly more pairs than
-    the mean: split so that parts of the longest match the mean.  With more
-    workgroups than CUs the longest-first order already balances them, and
-    the partial sums only add traffic (measured on MI355X: 4 x 2k D=64 MHA
-    0.114 -> 0.107 ms and one 8k D=128 GQA sequence 5.82 -> 3.69 ms with two
-    parts; the varlen batch, 464 workgroups, 1.62 -> 1.65 ms).  Never for
-    windows (short key blocks; the split kernel has no window
-    specialisation)."""
+    """How many workgroups to split each key block's pair loop over: 1 unless
+    the longest key block holds clearly more pairs than a CU's share of the
+    whole problem (the workgroups run longest first, so that block then sets
+    the kernel's time), else enough parts to bring it to that share.  Measured
+    on MI355X (backward with atomic dQ, 1 -> chosen parts): one 8k D=128 GQA
+    sequence 5.85 -> 3.77 ms, the varlen batch 1.43 -> 1.20 ms, 4 x 2k D=64
+    MHA 0.113 -> 0.111 ms; where the rule keeps 1 the split measured slower
+    (4 x 4k MHA 0.30 -> 0.36 ms).  Never for windows (short key blocks; the
+    split kernel has no window specialisation)."""
     if shape.window > 0:
         return 1
     pairs = pairs_per_key_block(shape, lengths)
-    if not pairs or len(pairs) * shape.hkv > _CUS:
+    if not pairs:
         return 1
-    mean = sum(pairs) / len(pairs)
+    per_cu = sum(pairs) * shape.hkv / _CUS
     longest = max(pairs)
-    if longest <= 1.25 * mean:
+    if longest <= 1.25 * per_cu:
         return 1
-    return int(min(MAX_SPLIT, -(-longest // max(mean, 1.0))))
+    return int(min(MAX_SPLIT, -(-longest // max(per_cu, 1.0))))
 
 
 def _split_workspace(inp: Inputs, ws: Workspace, nsplit: int) -> torch.Tensor:
