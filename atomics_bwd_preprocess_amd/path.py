@@ -126,15 +126,17 @@ def select_mode(shape: Shape, lengths=None) -> str:
     """"deterministic" (query-stationary dQ) or "atomic", whichever measured
     faster on MI355X for this kind of shape.  Backward times of both paths
     (preprocess through dQ), one MI355X:
-      D = 128: query-stationary faster up to ~1.5k keys per query (0.89x at
+      D = 128: query-stationary faster up to ~1k keys per query (0.89x at
       512, 0.90x at 1024, 1.02x at 2048, 1.07x at 4096) and with every window
-      measured (W = 128 .. 2048: 0.88x - 0.98x);
+      measured (W = 128 .. 2048: 0.88x - 0.98x); the ragged varlen batch
+      (~1.2k keys per query) runs faster with atomics once its key blocks are
+      ranked longest first and split (1.20 vs 1.30 ms);
       D = 64: atomic faster without a window (1.24x at 512 keys per query,
       1.08x at 1024); with a window query-stationary is faster up to
       W ~ 1k (0.93x at 128, 0.98x at 512, 1.01x at 2048)."""
     kq = keys_per_query(shape, lengths)
     if shape.head_dim == 128:
-        return "deterministic" if (shape.window > 0 or kq <= 1536) else "atomic"
+        return "deterministic" if (shape.window > 0 or kq <= 1024) else "atomic"
     return "deterministic" if 0 < shape.window <= 1024 else "atomic"
 
 

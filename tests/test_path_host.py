@@ -39,7 +39,7 @@ def test_keys_per_query_without_lengths_assumes_a_dense_batch():
     ("mha_causal", dict(n=32768), "atomic"),       # D=64 dense causal
     ("mha_causal", dict(n=1024), "atomic"),
     ("long_gqa", {}, "atomic"),                    # D=128, 16k keys per query
-    ("varlen_gqa", {}, "deterministic"),           # D=128, ~1.2k keys per query
+    ("varlen_gqa", {}, "atomic"),                  # D=128, ~1.2k keys per query
     ("sink_window", {}, "deterministic"),          # D=128, W=128
     ("mha_causal", dict(n=8192, window=128), "deterministic"),
     ("mha_causal", dict(n=8192, window=2048), "atomic"),
