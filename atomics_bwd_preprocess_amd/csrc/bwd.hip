@@ -87,7 +87,8 @@ struct Cfg {
   static constexpr int DS_OFF = DO_OFF + 2 * QT;
   // lse / Delta rows of a pair: at D = 128 they are copied raw into LDS
   // (64 floats per buffer, one wave each); otherwise they pass through
-  // registers and are stored as lse * log2(e) (+inf on rows past the end).
+  // registers and are stored as lse * log2(e) (+inf on rows past the end)
+  // and -Delta, which then seeds the dP accumulator.
   static constexpr bool LSE_DMA = D == 128;
   static constexpr int LSE_OFF = DS_OFF + 2 * DST;
   static constexpr int DLT_OFF = LSE_OFF + 2 * 64 * 4;
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
       // rows outside the sequence (or that saw nothing) get P = 0
       const float l2 = (tid >= prows || plse == -INFINITY) ? INFINITY : plse * kLog2e;
       reinterpret_cast<float*>(smem + C::LSE_OFF)[buf * 64 + tid] = l2;
-      reinterpret_cast<float*>(smem + C::DLT_OFF)[buf * 64 + tid] = pdlt;
+      reinterpret_cast<float*>(smem + C::DLT_OFF)[buf * 64 + tid] = -pdlt;
     }
   };
 
@@ -424,11 +425,23 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
         continue;
       }
       // -- S = Q K^T and dP = dO V^T: [BM queries] x [32 keys]
+      // With -Delta in LDS (register path) the dP accumulator starts from it,
+      // so the products leave dP - Delta without a subtraction per element.
+      // Register 4 g4 + e of a tile holds query row 32 mt + 8 g4 + 4 c + e.
       f32x16 sacc[MT], pacc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         sacc[mt] = f32x16{};
-        pacc[mt] = f32x16{};
+        if constexpr (C::LSE_DMA) {
+          pacc[mt] = f32x16{};
+        } else {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 nd = *reinterpret_cast<const f32x4*>(dlt + 32 * mt + 8 * g4 + 4 * c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pacc[mt][4 * g4 + e] = nd[e];
+          }
+        }
       }
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
@@ -468,14 +481,15 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
         for (int g4 = 0; g4 < 4; ++g4) {
           const int qr = 32 * mt + 8 * g4 + 4 * c;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + qr);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt + qr);
+          f32x4 d4 = {0.f, 0.f, 0.f, 0.f};  // Delta still to subtract (raw copies only)
+          if constexpr (C::LSE_DMA) d4 = *reinterpret_cast<const f32x4*>(dlt + qr);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g4 + e;
             const float l2 = C::LSE_DMA ? l4[e] * kLog2e : l4[e];
             const float pv = fast_exp2(sacc[mt][r] * p.scale_log2 - l2);
             sacc[mt][r] = pv;
-            pacc[mt][r] = pv * (pacc[mt][r] - d4[e]);
+            pacc[mt][r] = C::LSE_DMA ? pv * (pacc[mt][r] - d4[e]) : pv * pacc[mt][r];
           }
         }
       }
