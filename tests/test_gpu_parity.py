@@ -82,6 +82,10 @@ EDGE = [
     ("one_past_tiles", ai.workload("long_gqa").with_(seqlens=(257, 33), hq=8, hkv=2)),
     ("d128_noncausal_sink_bf16", ai.workload("tiny_gqa").with_(seqlens=(97, 160), d=128,
                                                                sink=True, dtype="bf16")),
+    # more (sequence, key block) items than the in-kernel longest-first ranking
+    # takes (520 > 512): the fixed key-block-slowest order
+    ("many_short_seqs", ai.workload("varlen_gqa").with_(
+        draw_lengths=None, seqlens=tuple(1 + (7 * i) % 19 for i in range(520)), hq=2, hkv=1)),
 ]
 
 
