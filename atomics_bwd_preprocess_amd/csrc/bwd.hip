@@ -58,6 +58,8 @@
 // which writes its fp32 dK / dV partial to a workspace slot of its own (no
 // atomics; a reduce pass sums the slots in a fixed order and casts), for
 // problems whose longest key block would otherwise set the critical path.
+// The windowed dK / dV-only variant runs four waves (128 keys) per
+// workgroup, two workgroups per CU (see nw_of).
 #include <limits.h>
 
 #include "common.h"
@@ -67,13 +69,21 @@ namespace attn {
 
 namespace {
 
-constexpr int kNW = 8;               // waves per workgroup (2 per SIMD)
-constexpr int kKT = 1;               // 32-key MFMA tiles per wave
-constexpr int kThreads = 64 * kNW;
-constexpr int kBN = kNW * 32 * kKT;  // keys per workgroup
+constexpr int kKT = 1;  // 32-key MFMA tiles per wave
+// Waves per workgroup: eight (two per SIMD, one workgroup per CU) in every
+// variant but the windowed dK / dV-only pass, which runs four, two
+// workgroups per CU.  Under a narrow window only about five of eight 32-key
+// tiles see a given query block, so with eight waves one SIMD holds two busy
+// waves on every pair while the others idle at the pair's barrier; two
+// four-wave workgroups share each SIMD without a common barrier, and one
+// fills the other's idle pairs.
+constexpr int nw_of(bool win, bool dq, bool split) { return win && !dq && !split ? 4 : 8; }
+constexpr int kNW = 8;  // the atomic pass
 
-template <int D>
+template <int D, int NW = kNW, bool DQ = true>
 struct Cfg {
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int BN = NW * 32 * kKT;       // keys per workgroup
   static constexpr int BM = D == 128 ? 32 : 64;  // query rows per pair
   static constexpr int MT = BM / 32;             // 32-row query tiles
   static constexpr int NT = D / 32;              // 32-wide dim tiles
@@ -81,16 +91,17 @@ struct Cfg {
   // LDS map (bytes)
   static constexpr int K_OFF = 0;
   static constexpr int QT = BM * D * 2;
-  static constexpr int Q_OFF = K_OFF + kBN * D * 2;
+  static constexpr int Q_OFF = K_OFF + BN * D * 2;
   static constexpr int DO_OFF = Q_OFF + 2 * QT;
-  static constexpr int DST = kBN * BM * 2;
+  static constexpr int DST = BN * BM * 2;
   static constexpr int DS_OFF = DO_OFF + 2 * QT;
   // lse / Delta rows of a pair: at D = 128 they are copied raw into LDS
   // (64 floats per buffer, one wave each); otherwise they pass through
   // registers and are stored as lse * log2(e) (+inf on rows past the end)
   // and -Delta, which then seeds the dP accumulator.
   static constexpr bool LSE_DMA = D == 128;
-  static constexpr int LSE_OFF = DS_OFF + 2 * DST;
+  // (the four-wave dK / dV-only pass has no dS tiles and leaves no room for them)
+  static constexpr int LSE_OFF = DS_OFF + (DQ || NW == 8 ? 2 * DST : 0);
   static constexpr int DLT_OFF = LSE_OFF + 2 * 64 * 4;
   // The last VLDS k-steps of each wave's V operand live in LDS (16 bytes per
   // lane per step, lane-linear) instead of registers: at D = 128 the
@@ -98,13 +109,13 @@ struct Cfg {
   static constexpr int VLDS = D == 128 ? 3 : 0;
   static constexpr int VREG = D / 16 - VLDS;  // V k-steps held in registers
   static constexpr int V_OFF = DLT_OFF + 2 * 64 * 4;
-  static constexpr int BYTES = V_OFF + VLDS * kNW * 1024;
+  static constexpr int BYTES = V_OFF + VLDS * NW * 1024;
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
-  static constexpr int PF = BM * CH / kThreads;      // prefetch chunks per thread per tensor
+  static constexpr int PF = BM * CH / THREADS;       // prefetch chunks per thread per tensor
   static constexpr int NQT = BM / 16, NDT = D / 16;  // 16x16 dQ tiles
-  static_assert(NQT * NDT == 2 * kNW, "two 16x16 dQ tiles per wave");
-  static_assert(PF >= 1 && BM * CH % kThreads == 0, "prefetch split");
-  static_assert(BYTES <= 160 * 1024, "LDS budget");
+  static_assert(!DQ || NQT * NDT == 2 * NW, "two 16x16 dQ tiles per wave");
+  static_assert(PF >= 1 && BM * CH % THREADS == 0, "prefetch split");
+  static_assert(BYTES * (8 / NW) <= 160 * 1024, "LDS budget (8 / NW workgroups per CU)");
 };
 
 struct BwdArgs {
@@ -133,17 +144,17 @@ struct BwdArgs {
 // workgroup ranks the num_seqs * nkb (sequence, key block) items by their
 // number of query blocks under the masks (ties: lower item first; empty
 // items last) and takes the item of rank r.  All threads take part; it uses
-// the start of LDS and ends with a barrier.  At most kMaxLpt items (one per
-// thread, then a scan of LDS broadcasts).
-constexpr int kMaxLpt = kThreads;
-template <int BM>
+// the start of LDS and ends with a barrier.  At most one item per thread
+// (64 NW for NW waves), then a scan of LDS broadcasts.
+template <int BM, int NW>
 __device__ int lpt_item(const BwdArgs& p, int nkb, int r, char* smem) {
+  constexpr int BN = NW * 32 * kKT;
   int* work = reinterpret_cast<int*>(smem);
-  int* found = work + kMaxLpt;
+  int* found = work + 64 * NW;
   const int n = p.num_seqs * nkb, i = threadIdx.x;
   int wi = -1;
   if (i < n) {
-    const int s = i / nkb, kv0 = (i % nkb) * kBN;
+    const int s = i / nkb, kv0 = (i % nkb) * BN;
     int a, b;
     seq_bounds(p.cu, s, p.max_seqlen, p.total, a, b);
     const int L = b - a;
@@ -151,7 +162,7 @@ __device__ int lpt_item(const BwdArgs& p, int nkb, int r, char* smem) {
     if (kv0 < L) {
       const int ib0 = p.causal ? kv0 / BM : 0;
       int ib1 = (L + BM - 1) / BM;
-      if (p.window > 0) ib1 = min(ib1, (min(L, kv0 + kBN) - 1 + p.window - 1) / BM + 1);
+      if (p.window > 0) ib1 = min(ib1, (min(L, kv0 + BN) - 1 + p.window - 1) / BM + 1);
       wi = ib1 - ib0;
     }
     work[i] = wi;
@@ -193,8 +204,10 @@ __device__ __forceinline__ int dst_off(int r, int q) {  // q: multiple of 4
 // BHSD: [B, H, S, D] tensors instead of packed [T, H, D].
 // SPLIT: pairs of a key block split over p.nsplit workgroups (see above).
 template <typename T, int D, bool WIN, bool DQ, bool BHSD, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
-  using C = Cfg<D>;
+__global__ __launch_bounds__(64 * nw_of(WIN, DQ, SPLIT), 8 / nw_of(WIN, DQ, SPLIT)) void bwd_kernel(BwdArgs p) {
+  constexpr int NW = nw_of(WIN, DQ, SPLIT);
+  using C = Cfg<D, NW, DQ>;
+  constexpr int kThreads = C::THREADS, kBN = C::BN;
   using T8 = typename V8<T>::type;
   using T4 = typename V8<T>::half_type;
   constexpr int BM = C::BM, MT = C::MT, NT = C::NT;
@@ -218,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     const int r = blockIdx.x / (p.hkv * (SPLIT ? p.nsplit : 1));
     if constexpr (SPLIT) part = (blockIdx.x / p.hkv) % p.nsplit;
     g = blockIdx.x % p.hkv;
-    const int item = uni(lpt_item<BM>(p, nkb, r, smem));
+    const int item = uni(lpt_item<BM, NW>(p, nkb, r, smem));
     s = item / nkb;
     jb = item % nkb;
   } else {
@@ -272,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
       if (ks < C::VREG)
         vreg[kt][ks] = __builtin_bit_cast(T8, buf_load16(vr, off));
       else
-        lds_dma16(vr, smem + C::V_OFF + ((kt * C::VLDS + ks - C::VREG) * kNW + uni(w)) * 1024, off);
+        lds_dma16(vr, smem + C::V_OFF + ((kt * C::VLDS + ks - C::VREG) * NW + uni(w)) * 1024, off);
       if constexpr (C::KREG) kreg[kt][ks] = __builtin_bit_cast(T8, buf_load16(kr, off));
     }
   }
@@ -315,12 +328,12 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
     const rsrc_t dr = make_rsrc(static_cast<const T*>(p.dout) + qb, rows * q_row * 2);
 #pragma unroll
     for (int u = 0; u < C::PF; ++u) {
-      // Lane l of wave w fills physical chunk P = 64 (w + kNW u) + l of the
+      // Lane l of wave w fills physical chunk P = 64 (w + NW u) + l of the
       // swizzled tile, i.e. row P / CH, logical chunk (P % CH) ^ swz(row).
       // Rows past the sequence end repeat the last row; P = dS = 0 there
       // whatever Q / dO hold (their lse is stored as +inf, or, when lse is
       // copied raw, the edge-tile pass masks them).
-      const int P0 = uni(64 * (w + kNW * u));  // wave-uniform
+      const int P0 = uni(64 * (w + NW * u));  // wave-uniform
       const int P = P0 + lane;
       const int r = P / C::CH, ch = (P % C::CH) ^ chunk_swz<D>(r);
       const uint32_t off = ((uint32_t)min(r, rows - 1) * q_row + 8 * ch) * 2;
@@ -456,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
           sacc[mt] = mfma32(lds16<T>(qs, o), kb, sacc[mt]);
           const T8 vb = ks < C::VREG
                             ? vreg[kt][ks]
-                            : lds16<T>(smem, C::V_OFF + ((kt * C::VLDS + ks - C::VREG) * kNW + w) * 1024 + 16 * lane);
+                            : lds16<T>(smem, C::V_OFF + ((kt * C::VLDS + ks - C::VREG) * NW + w) * 1024 + 16 * lane);
           pacc[mt] = mfma32(lds16<T>(dos, o), vb, pacc[mt]);
         }
       }
@@ -664,8 +677,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs p) {
 }
 
 template <typename T, int D, bool DQ, bool BHSD>
-hipError_t bwd_t2(const BwdArgs& args, unsigned blocks, hipStream_t stream) {
-  const dim3 grid(blocks), block(kThreads);
+hipError_t bwd_t2(const BwdArgs& args, unsigned blocks, int threads, hipStream_t stream) {
+  const dim3 grid(blocks), block(threads);
   // The split kernel is built without the window specialisation (it is
   // still correct for windows, whose key blocks are short anyway).
   if (args.dkv_part)
@@ -678,10 +691,10 @@ hipError_t bwd_t2(const BwdArgs& args, unsigned blocks, hipStream_t stream) {
 }
 
 template <typename T, int D, bool DQ>
-hipError_t bwd_t(const BwdArgs& args, int nkb, bool bhsd, hipStream_t stream) {
+hipError_t bwd_t(const BwdArgs& args, int nkb, int threads, bool bhsd, hipStream_t stream) {
   const unsigned blocks = (unsigned)nkb * args.num_seqs * args.hkv * (unsigned)args.nsplit;
-  return bhsd ? bwd_t2<T, D, DQ, true>(args, blocks, stream)
-              : bwd_t2<T, D, DQ, false>(args, blocks, stream);
+  return bhsd ? bwd_t2<T, D, DQ, true>(args, blocks, threads, stream)
+              : bwd_t2<T, D, DQ, false>(args, blocks, threads, stream);
 }
 
 template <bool DQ>
@@ -711,15 +724,20 @@ hipError_t bwd_dispatch(const Problem& p, const void* q, const void* k, const vo
   a.scale_log2 = p.scale * kLog2e;
   a.dkv_part = dkv_part;
   a.nsplit = nsplit;
-  const int nkb = (p.max_seqlen + kBN - 1) / kBN;
+  // The variant bwd_t2 picks (split, else windowed, else plain) fixes the
+  // workgroup: nw_of waves, 32 keys each.
+  const int nw = nw_of(p.window > 0, DQ, dkv_part != nullptr);
+  const int bn = nw * 32 * kKT;
+  const int nkb = (p.max_seqlen + bn - 1) / bn;
   // Packed sequences of unknown (device-side) lengths are ranked in the
-  // kernel; a dense batch's formula order is already longest first.
-  a.lpt = (cu != nullptr && p.num_seqs > 1 && (long long)p.num_seqs * nkb <= kMaxLpt) ? 1 : 0;
+  // kernel (one item per thread at most); a dense batch's formula order is
+  // already longest first.
+  a.lpt = (cu != nullptr && p.num_seqs > 1 && (long long)p.num_seqs * nkb <= 64LL * nw) ? 1 : 0;
   if (p.bf16)
-    return p.d == 64 ? bwd_t<__bf16, 64, DQ>(a, nkb, p.bhsd, stream)
-                     : bwd_t<__bf16, 128, DQ>(a, nkb, p.bhsd, stream);
-  return p.d == 64 ? bwd_t<_Float16, 64, DQ>(a, nkb, p.bhsd, stream)
-                   : bwd_t<_Float16, 128, DQ>(a, nkb, p.bhsd, stream);
+    return p.d == 64 ? bwd_t<__bf16, 64, DQ>(a, nkb, 64 * nw, p.bhsd, stream)
+                     : bwd_t<__bf16, 128, DQ>(a, nkb, 64 * nw, p.bhsd, stream);
+  return p.d == 64 ? bwd_t<_Float16, 64, DQ>(a, nkb, 64 * nw, p.bhsd, stream)
+                   : bwd_t<_Float16, 128, DQ>(a, nkb, 64 * nw, p.bhsd, stream);
 }
 
 }  // namespace
