@@ -58,7 +58,7 @@
 // which writes its fp32 dK / dV partial to a workspace slot of its own (no
 // atomics; a reduce pass sums the slots in a fixed order and casts), for
 // problems whose longest key block would otherwise set the critical path.
-// The windowed dK / dV-only variant runs four waves (128 keys) per
+// The unsplit dK / dV-only variants run four waves (128 keys) per
 // workgroup, two workgroups per CU (see nw_of).
 #include <limits.h>
 
@@ -70,14 +70,17 @@ namespace attn {
 namespace {
 
 constexpr int kKT = 1;  // 32-key MFMA tiles per wave
-// Waves per workgroup: eight (two per SIMD, one workgroup per CU) in every
-// variant but the windowed dK / dV-only pass, which runs four, two
-// workgroups per CU.  Under a narrow window only about five of eight 32-key
-// tiles see a given query block, so with eight waves one SIMD holds two busy
-// waves on every pair while the others idle at the pair's barrier; two
-// four-wave workgroups share each SIMD without a common barrier, and one
-// fills the other's idle pairs.
-constexpr int nw_of(bool win, bool dq, bool split) { return win && !dq && !split ? 4 : 8; }
+// Waves per workgroup: eight (two per SIMD, one workgroup per CU), except in
+// the unsplit dK / dV-only pass, which runs four, two workgroups per CU.
+// Where only some of a key block's 32-key tiles see a query block (the
+// causal diagonal; under a narrow window about five of eight on every
+// pair), eight waves leave SIMDs idle at the pair's barrier while one SIMD
+// holds two busy waves; two four-wave workgroups share each SIMD without a
+// common barrier, so one fills the other's idle pairs, and short sequences
+// get twice as many workgroups.  The atomic pass keeps 256 keys per
+// workgroup (its atomic bytes scale with 1 / keys per workgroup), and the
+// split pass keeps eight waves as well.
+constexpr int nw_of(bool dq, bool split) { return !dq && !split ? 4 : 8; }
 constexpr int kNW = 8;  // the atomic pass
 
 template <int D, int NW = kNW, bool DQ = true>
@@ -204,8 +207,8 @@ __device__ __forceinline__ int dst_off(int r, int q) {  // q: multiple of 4
 // BHSD: [B, H, S, D] tensors instead of packed [T, H, D].
 // SPLIT: pairs of a key block split over p.nsplit workgroups (see above).
 template <typename T, int D, bool WIN, bool DQ, bool BHSD, bool SPLIT>
-__global__ __launch_bounds__(64 * nw_of(WIN, DQ, SPLIT), 8 / nw_of(WIN, DQ, SPLIT)) void bwd_kernel(BwdArgs p) {
-  constexpr int NW = nw_of(WIN, DQ, SPLIT);
+__global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void bwd_kernel(BwdArgs p) {
+  constexpr int NW = nw_of(DQ, SPLIT);
   using C = Cfg<D, NW, DQ>;
   constexpr int kThreads = C::THREADS, kBN = C::BN;
   using T8 = typename V8<T>::type;
@@ -724,9 +727,8 @@ hipError_t bwd_dispatch(const Problem& p, const void* q, const void* k, const vo
   a.scale_log2 = p.scale * kLog2e;
   a.dkv_part = dkv_part;
   a.nsplit = nsplit;
-  // The variant bwd_t2 picks (split, else windowed, else plain) fixes the
-  // workgroup: nw_of waves, 32 keys each.
-  const int nw = nw_of(p.window > 0, DQ, dkv_part != nullptr);
+  // The variant bwd_t2 picks fixes the workgroup: nw_of waves, 32 keys each.
+  const int nw = nw_of(DQ, dkv_part != nullptr);
   const int bn = nw * 32 * kKT;
   const int nkb = (p.max_seqlen + bn - 1) / bn;
   // Packed sequences of unknown (device-side) lengths are ranked in the
