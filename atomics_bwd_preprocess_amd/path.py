@@ -125,19 +125,20 @@ def keys_per_query(shape: Shape, lengths=None) -> float:
 def select_mode(shape: Shape, lengths=None) -> str:
     """"deterministic" (query-stationary dQ) or "atomic", whichever measured
     faster on MI355X for this kind of shape.  Backward times of both paths
-    (preprocess through dQ), one MI355X:
-      D = 128: query-stationary faster up to ~1k keys per query (0.89x at
-      512, 0.90x at 1024, 1.02x at 2048, 1.07x at 4096) and with every window
-      measured (W = 128 .. 2048: 0.88x - 0.98x); the ragged varlen batch
+    (preprocess through dQ, deterministic / atomic), one MI355X:
+      D = 128: query-stationary faster up to ~1k keys per query (0.80x at
+      512, 0.87x at 1024, 1.03x at 2048, 1.11x at 4096) and with every window
+      measured (W = 128 .. 2048: 0.72x - 0.96x); the ragged varlen batch
       (~1.2k keys per query) runs faster with atomics once its key blocks are
-      ranked longest first and split (1.20 vs 1.30 ms);
-      D = 64: atomic faster without a window (1.24x at 512 keys per query,
-      1.08x at 1024); with a window query-stationary is faster up to
-      W ~ 1k (0.93x at 128, 0.98x at 512, 1.01x at 2048)."""
+      ranked longest first and split;
+      D = 64: atomic faster without a window (1.22x at 512 keys per query,
+      1.06x at 1024, 1.05x at 2048); with a window query-stationary is
+      faster up to the largest measured, W = 2048 (0.81x at 128, 0.88x at
+      512, 0.94x at 2048)."""
     kq = keys_per_query(shape, lengths)
     if shape.head_dim == 128:
         return "deterministic" if (shape.window > 0 or kq <= 1024) else "atomic"
-    return "deterministic" if 0 < shape.window <= 1024 else "atomic"
+    return "deterministic" if 0 < shape.window <= 2048 else "atomic"
 
 
 # Workgroup geometry of the key/value-stationary pass (bwd.hip): 256 keys per

@@ -42,7 +42,8 @@ def test_keys_per_query_without_lengths_assumes_a_dense_batch():
     ("varlen_gqa", {}, "atomic"),                  # D=128, ~1.2k keys per query
     ("sink_window", {}, "deterministic"),          # D=128, W=128
     ("mha_causal", dict(n=8192, window=128), "deterministic"),
-    ("mha_causal", dict(n=8192, window=2048), "atomic"),
+    ("mha_causal", dict(n=8192, window=2048), "deterministic"),
+    ("mha_causal", dict(n=8192, window=4096), "atomic"),
 ])
 def test_select_mode_follows_the_measured_crossover(name, kw, mode):
     w = ai.workload(name, **kw)
