@@ -50,7 +50,7 @@ def _case(i):
     return w, layout, mode, splits
 
 
-CASES = list(range(24))
+CASES = list(range(48))
 
 
 @pytest.mark.parametrize("i", CASES)
