@@ -297,10 +297,36 @@ def auto_entry(x: dict, r: dict) -> dict:
             "bwd_tflops": round(bwd_flops(x) / (r["auto_ms"] * 1e-3) / 1e12, 2)}
 
 
-def cpu_baseline(x: dict, min_run_s: float = 4.0) -> dict:
+def oracle_sample(x: dict, n_s: int, nh: int) -> dict:
+    """The sub-problem the CPU baseline times: the first n_s rows of the
+    packed batch as one sequence (the first sequence's rows when it is at
+    least n_s long), for query heads [0, nh) and the kv heads they read.
+    Query head h reads kv head h // G; below one group every head reads kv
+    head 0, and above it the sample keeps whole groups (nh rounded up), so
+    the oracle's own grouping (hq / hkv heads per kv head) is the
+    workload's."""
+    g = x["hq"] // x["hkv"]
+    if nh > g:
+        nh = min(x["hq"], -(-nh // g) * g)
+    nkv = -(-nh // g)
+    sub = dict(x)
+    sub["q"] = x["q"][:n_s, :nh]
+    sub["do"] = x["do"][:n_s, :nh]
+    sub["k"] = x["k"][:n_s, :nkv]
+    sub["v"] = x["v"][:n_s, :nkv]
+    sub["sink"] = None if x["sink"] is None else x["sink"][:nh]
+    sub["cu_seqlens"] = np.array([0, n_s], dtype=np.int32)
+    sub["lengths"] = [n_s]
+    sub["hq"], sub["hkv"] = nh, nkv
+    return sub
+
+
+def cpu_baseline(x: dict, min_run_s: float = 10.0) -> dict:
     """The fp64 oracle (as it stands) on a bounded sample of the workload:
-    one (sequence, query head) of length n_s with its kv head, n_s doubled
-    until one run takes >= min_run_s or reaches the workload's length."""
+    the first sequence's first n_s rows for the first nh query heads (with
+    their kv heads), n_s doubled up to the workload's length and then nh
+    doubled, until one run takes >= min_run_s or covers the whole sequence
+    and every head."""
     from oracle import attention as orc
 
     try:
@@ -310,29 +336,26 @@ def cpu_baseline(x: dict, min_run_s: float = 4.0) -> dict:
     except Exception:  # pragma: no cover
         threads = 1
     n_max = max(x["lengths"])
-    n_s = min(1024, n_max)
+    n_s, nh = min(1024, n_max), 1
     while True:
-        sub = dict(x)
-        sub["q"] = x["q"][:n_s, :1]
-        sub["do"] = x["do"][:n_s, :1]
-        sub["k"] = x["k"][:n_s, :1]
-        sub["v"] = x["v"][:n_s, :1]
-        sub["sink"] = None if x["sink"] is None else x["sink"][:1]
-        sub["cu_seqlens"] = np.array([0, n_s], dtype=np.int32)
-        sub["lengths"] = [n_s]
-        sub["hq"] = sub["hkv"] = 1
+        sub = oracle_sample(x, n_s, nh)
+        nh = sub["hq"]
         t0 = time.perf_counter()
         orc.forward_backward(sub)
         dt = time.perf_counter() - t0
-        if dt >= min_run_s or n_s >= n_max:
+        if dt >= min_run_s or (n_s >= n_max and nh >= x["hq"]):
             break
-        n_s = min(n_max, 2 * n_s)
+        if n_s < n_max:
+            n_s = min(n_max, 2 * n_s)
+        else:
+            nh = min(x["hq"], 2 * nh)
     flops = bwd_flops(sub)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": (f"fp64 numpy oracle forward+backward, 1 sequence x 1 head of length {n_s} "
-                       f"(D={x['d']}, causal={x['causal']}, window={x['window']}) taking "
-                       f"{dt:.2f} s; rate = backward FLOPs of that sample / its wall time")}
+            "sample": (f"fp64 numpy oracle forward+backward, 1 sequence of length {n_s} x "
+                       f"{sub['hq']} query head(s) / {sub['hkv']} kv head(s) (D={x['d']}, "
+                       f"causal={x['causal']}, window={x['window']}) taking {dt:.2f} s; rate = "
+                       f"backward FLOPs of that sample / its wall time")}
 
 
 def describe(name: str, x: dict) -> dict:

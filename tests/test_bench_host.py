@@ -65,3 +65,34 @@ def test_headline_atomic_bytes():
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+@pytest.mark.parametrize("nh", [1, 2, 3, 4, 5, 6])
+def test_oracle_sample_keeps_the_head_grouping(nh):
+    # The CPU baseline's sample of query heads [0, nh) must be the same
+    # problem as those heads of the full workload (group size 3 here, so
+    # nh = 4 or 5 only works as whole groups).
+    import numpy as np
+
+    import attn_inputs as ai
+    from oracle import attention as orc
+
+    w = ai.workload("sink_window").with_(seqlens=(24,), hq=6, hkv=2, d=64, window=9)
+    x = ai.generate(w, 0)
+    sub = bench.oracle_sample(x, 24, nh)
+    assert sub["hq"] >= nh and sub["hq"] % sub["hkv"] == 0
+    assert sub["hq"] <= 3 or sub["hq"] % 3 == 0
+    full, part = orc.forward_backward(x), orc.forward_backward(sub)
+    h = sub["hq"]
+    np.testing.assert_allclose(part["dq"], full["dq"][:, :h], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(part["lse"], full["lse"][:h], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(part["dsink"], full["dsink"][:h], rtol=1e-12, atol=1e-12)
+
+
+def test_cpu_baseline_covers_the_workload_when_given_time():
+    import attn_inputs as ai
+
+    w = ai.workload("tiny_gqa")
+    r = bench.cpu_baseline(ai.generate(w, 0), min_run_s=1e9)
+    assert r["kind"] == "oracle" and r["value"] > 0
+    assert f"length {w.seqlens[0]} x {w.hq} query head(s) / {w.hkv} kv head(s)" in r["sample"]
