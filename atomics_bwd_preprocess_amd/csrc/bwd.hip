@@ -417,15 +417,17 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
       // Keys [tk_lo, tk_lo + 32) of this wave's tile kt against queries [q0, q0 + BM).
       const int tk_lo = wk_lo + 32 * kt, tk_hi = tk_lo + 31;
       // Every path through the tile issues all 8 pending atomics of the
-      // previous pair (the barrier's wait count relies on it).
+      // previous pair (the barrier's wait count relies on it).  On the first
+      // pair they hold zeros aimed at an empty range and are dropped; issuing
+      // them anyway keeps the products and the exponentials in one block.
       if constexpr (TRICKLE) {
-        if (kt == 0 && j > 0) flush(0, 2);
+        if (kt == 0) flush(0, 2);
       }
       const bool empty = tk_lo >= L || q0 >= L || (p.causal && tk_lo > q0 + BM - 1) ||
                          (p.window > 0 && tk_hi <= q0 - p.window);
       if (empty) {
         if constexpr (TRICKLE) {
-          if (kt == 0 && j > 0) flush(2, 4);
+          if (kt == 0) flush(2, 4);
         }
         // With WIN the dQ product below skips exactly the key tiles that no
         // query of the block can see, so their dS rows are never read;
@@ -459,69 +461,89 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
           }
         }
       }
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
+      auto prod_step = [&](int mt, int ks) {
         T8 kb;
         if constexpr (C::KREG)
           kb = kreg[kt][ks];
         else
           kb = lds16<T>(smem, C::K_OFF + rm_off<D>(32 * kKT * w + 32 * kt + n, 16 * ks + 8 * c));
+        const int o = rm_off<D>(32 * mt + n, 16 * ks + 8 * c);
+        sacc[mt] = mfma32(lds16<T>(qs, o), kb, sacc[mt]);
+        const T8 vb = ks < C::VREG
+                          ? vreg[kt][ks]
+                          : lds16<T>(smem, C::V_OFF + ((kt * C::VLDS + ks - C::VREG) * NW + w) * 1024 + 16 * lane);
+        pacc[mt] = mfma32(lds16<T>(dos, o), vb, pacc[mt]);
+      };
+      // -- P = exp2(S scale log2e - lse log2e); dS' = P (dP - Delta) for the
+      //    four rows of group g4 of query tile mt.  The factor `scale` of dS
+      //    is applied once to dK (epilogue) and to dQ (postprocess), not per
+      //    element.
+      auto expq = [&](int mt, int g4) {
+        const int qr = 32 * mt + 8 * g4 + 4 * c;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + qr);
+        f32x4 d4 = {0.f, 0.f, 0.f, 0.f};  // Delta still to subtract (raw copies only)
+        if constexpr (C::LSE_DMA) d4 = *reinterpret_cast<const f32x4*>(dlt + qr);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int o = rm_off<D>(32 * mt + n, 16 * ks + 8 * c);
-          sacc[mt] = mfma32(lds16<T>(qs, o), kb, sacc[mt]);
-          const T8 vb = ks < C::VREG
-                            ? vreg[kt][ks]
-                            : lds16<T>(smem, C::V_OFF + ((kt * C::VLDS + ks - C::VREG) * NW + w) * 1024 + 16 * lane);
-          pacc[mt] = mfma32(lds16<T>(dos, o), vb, pacc[mt]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          const float l2 = C::LSE_DMA ? l4[e] * kLog2e : l4[e];
+          const float pv = fast_exp2(sacc[mt][r] * p.scale_log2 - l2);
+          sacc[mt][r] = pv;
+          pacc[mt][r] = C::LSE_DMA ? pv * (pacc[mt][r] - d4[e]) : pv * pacc[mt][r];
         }
-      }
-
-      // D = 64: the exponentials run at raised wave priority, so the two
-      // waves sharing a SIMD drift apart and one's matrix work overlaps the
-      // other's exponentials (measured +1.6 %; neutral or worse at D = 128).
-      if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
-      // -- P = exp2(S scale log2e - lse log2e); dS' = P (dP - Delta).  The
-      //    factor `scale` of dS is applied once to dK (epilogue) and to dQ
-      //    (postprocess), not per element.  Masks only on tiles that need them:
-      //    visible iff lo <= q - k <= hi, k < L and q < L.
-      const bool full = (q0 + BM <= L) && (tk_hi < L) && (!p.causal || tk_hi <= q0) &&
-                        (p.window <= 0 || tk_lo > q0 + BM - 1 - p.window);
-      const int kj = tk_lo + n;
-      const int dlo = p.causal ? 0 : INT_MIN;
-      const int dhi = p.window > 0 ? p.window - 1 : INT_MAX;
-      const int kin = kj < L ? 1 : 0;
+      };
+      if constexpr (MT == 2) {
+        // Two query tiles (D = 64): the second tile's S / dP products run
+        // under the first tile's exponentials (an LDS-read-only scheduling
+        // barrier per k-step keeps them interleaved), with the wave at raised
+        // priority from there to the dV / dK products, so the two waves
+        // sharing a SIMD also drift apart and one's matrix work overlaps the
+        // other's exponentials.  Measured on the dK / dV-only pass: 4-7 %
+        // faster than the products of both tiles first (atomic pass
+        // unchanged, atomic-bound).  Interleaving the second tile's
+        // exponentials with the first tile's dV / dK products as well was
+        // slower, at both head dims.
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+        for (int ks = 0; ks < D / 16; ++ks) prod_step(0, ks);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int qr = 32 * mt + 8 * g4 + 4 * c;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + qr);
-          f32x4 d4 = {0.f, 0.f, 0.f, 0.f};  // Delta still to subtract (raw copies only)
-          if constexpr (C::LSE_DMA) d4 = *reinterpret_cast<const f32x4*>(dlt + qr);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g4 + e;
-            const float l2 = C::LSE_DMA ? l4[e] * kLog2e : l4[e];
-            const float pv = fast_exp2(sacc[mt][r] * p.scale_log2 - l2);
-            sacc[mt][r] = pv;
-            pacc[mt][r] = C::LSE_DMA ? pv * (pacc[mt][r] - d4[e]) : pv * pacc[mt][r];
-          }
+        for (int ks = 0; ks < D / 16; ++ks) {
+          prod_step(1, ks);
+          expq(0, ks);
+          __builtin_amdgcn_sched_barrier(0x100);
         }
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) expq(1, g4);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) prod_step(mt, ks);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) expq(mt, g4);
       }
       if constexpr (TRICKLE) {
-        if (kt == 0 && j > 0) {
+        if (kt == 0) {
           __builtin_amdgcn_sched_barrier(0);
           flush(2, 4);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // Edge tiles: zero P and dS where the key is hidden.  Selecting (not
-      // multiplying) discards whatever the unmasked exponent produced there.
-      // The empty asm keeps this a real branch: if-converted, its compares
-      // and selects would run on every tile.
+      // Edge tiles: zero P and dS where the key is hidden (visible iff
+      // lo <= q - k <= hi, k < L and q < L).  Selecting (not multiplying)
+      // discards whatever the unmasked exponent produced there.  The empty asm
+      // keeps this a real branch: if-converted, its compares and selects would
+      // run on every tile.
+      const bool full = (q0 + BM <= L) && (tk_hi < L) && (!p.causal || tk_hi <= q0) &&
+                        (p.window <= 0 || tk_lo > q0 + BM - 1 - p.window);
       if (!full) {
         asm volatile("");
+        const int kj = tk_lo + n;
+        const int dlo = p.causal ? 0 : INT_MIN;
+        const int dhi = p.window > 0 ? p.window - 1 : INT_MAX;
+        const int kin = kj < L ? 1 : 0;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll

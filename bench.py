@@ -21,6 +21,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -90,7 +91,8 @@ def bwd_atomic_bytes(x: dict) -> float:
 def atomic_ceiling_gbs():
     """Live device-wide rate of device-scope fp32 atomic adds (GB/s of added
     data): 32768 waves each adding to a 256-byte segment per iteration over a
-    256 MiB buffer, timed with HIP events over three launches."""
+    256 MiB buffer, timed with HIP events over 20 launches after 0.3 s of
+    warm-up launches."""
     import ctypes
 
     import torch
@@ -101,11 +103,12 @@ def atomic_ceiling_gbs():
     f = lib.attn_microbench_atomic_rate
     f.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     f.restype = ctypes.c_int
-    nseg, blocks, iters, reps = 1 << 20, 8192, 64, 3
+    nseg, blocks, iters, reps = 1 << 20, 8192, 64, 20
     buf = torch.zeros(nseg * 64, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     if f(buf.data_ptr(), nseg, blocks, iters, stream.cuda_stream) != 0:
         return None
+    _warm(lambda: f(buf.data_ptr(), nseg, blocks, iters, stream.cuda_stream), 0, 0.3)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
@@ -204,7 +207,34 @@ def _traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
-def run_gpu(x: dict, steps: int, warmup: int, layout: str = "thd") -> dict:
+def _warm(fn, count: int, warm_s: float) -> float:
+    """Run fn `count` times, then keep running it until warm_s seconds have
+    passed (GPU clocks ramp up over a few hundred ms of load after the idle
+    host-side input generation; short workloads measured 5-12 % slow with a
+    fixed handful of warm-up steps).  Returns the wall time per call of the
+    time-based part (0 if none ran)."""
+    import torch
+
+    for _ in range(count):
+        fn()
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while time.perf_counter() - t0 < warm_s:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / n if n else 0.0
+
+
+def run_gpu(x: dict, steps: int, warmup: int, layout: str = "thd", warm_s: float = 0.0,
+            min_timed_s: float = 0.0) -> dict:
+    """HIP-event times of every launch of the path on x.  The first section
+    (forward, then the atomic backward) runs `warmup` untimed steps and then
+    `steps` timed ones; with warm_s > 0 every section also warms up for that
+    long first, and with min_timed_s > 0 the step count is raised (up to
+    400) until the timed steps take about that long."""
     import torch
 
     from atomics_bwd_preprocess_amd import (attn_bwd, attn_bwd_dkdv, attn_bwd_dq,
@@ -213,10 +243,10 @@ def run_gpu(x: dict, steps: int, warmup: int, layout: str = "thd") -> dict:
     inp = path.to_device(x, "cuda", layout=layout)
     ws = path.workspace(inp)
     stream = torch.cuda.current_stream()
+    per_step = _warm(lambda: path.step(inp, ws), warmup, warm_s)
+    if min_timed_s > 0 and per_step > 0:
+        steps = int(min(400, max(steps, math.ceil(min_timed_s / per_step))))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
-    for _ in range(warmup):
-        path.step(inp, ws)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         e = ev[i]
@@ -238,11 +268,10 @@ def run_gpu(x: dict, steps: int, warmup: int, layout: str = "thd") -> dict:
     out = dict(wall_ms_per_step=1e3 * wall / steps, fwd_ms=float(mean[0]), pre_ms=float(mean[1]),
                bwd_ms=float(mean[2]), post_ms=float(mean[3]),
                bwd_ms_min=float(ms[:, 2].min()), bwd_ms_median=float(np.median(ms[:, 2])))
+    out["steps"] = steps
     # The deterministic backward on the same inputs: preprocess without the
     # accumulator, the dK/dV-only main pass, the query-stationary dQ pass.
-    for _ in range(2):
-        path.backward(inp, ws, mode="deterministic")
-    torch.cuda.synchronize()
+    _warm(lambda: path.backward(inp, ws, mode="deterministic"), 2, warm_s)
     for i in range(steps):
         e = ev[i]
         e[0].record(stream)
@@ -260,9 +289,7 @@ def run_gpu(x: dict, steps: int, warmup: int, layout: str = "thd") -> dict:
                auto_mode=path.select_mode(inp.shape, inp.lengths),
                auto_splits=path.select_splits(inp.shape, inp.lengths))
     # The whole backward as path.backward(mode="auto", kv_splits="auto") runs it.
-    for _ in range(2):
-        path.backward(inp, ws, mode="auto", kv_splits="auto")
-    torch.cuda.synchronize()
+    _warm(lambda: path.backward(inp, ws, mode="auto", kv_splits="auto"), 2, warm_s)
     for i in range(steps):
         ev[i][0].record(stream)
         path.backward(inp, ws, mode="auto", kv_splits="auto")
@@ -403,13 +430,16 @@ def main(argv=None) -> int:
     w = ai.workload(args.workload, n=args.n) if args.workload == "mha_causal" else \
         ai.workload(args.workload)
     x = ai.generate(w, args.seed)
+    # The machine's own ceilings first (they also bring the clocks up after
+    # the host-side input generation); then the W warm-up and K timed steps.
+    ceiling = atomic_ceiling_gbs()
+    copy_gbs = copy_reference_gbs()
     r = run_gpu(x, args.steps, args.warmup)
     fl = bwd_flops(x)
     bwd_total_ms = r["pre_ms"] + r["bwd_ms"] + r["post_ms"]
     value = fl / (bwd_total_ms * 1e-3) / 1e12
     kernel_tflops = fl / (r["bwd_ms"] * 1e-3) / 1e12
     traffic = _traffic(w.name if w.name != "mha_causal" else f"mha_causal_n{args.n}")
-    ceiling = atomic_ceiling_gbs()
     pre_b, post_b = prepost_bytes(x)
     line = {
         "metric": METRIC,
@@ -437,7 +467,7 @@ def main(argv=None) -> int:
         "hbm_gbs": {"attn_bwd_preprocess": round(pre_b / (r["pre_ms"] * 1e-3) / 1e9, 1),
                     "attn_bwd_postprocess": round(post_b / (r["post_ms"] * 1e-3) / 1e9, 1),
                     "peak": PEAK_HBM_GBS,
-                    "copy_reference": round(copy_reference_gbs(), 1)},
+                    "copy_reference": round(copy_gbs, 1)},
         "fwd_tflops": round(fwd_flops(x) / (r["fwd_ms"] * 1e-3) / 1e12, 3),
         "atomics": {"kernel": "attn_bwd main kernel",
                     "bytes_per_launch": bwd_atomic_bytes(x),
@@ -468,7 +498,7 @@ def main(argv=None) -> int:
         for nm, n, layout in cases:
             wx = ai.workload(nm, n=n) if n else ai.workload(nm)
             xx = ai.generate(wx, args.seed)
-            rr = run_gpu(xx, max(3, args.steps // 4), 2, layout)
+            rr = run_gpu(xx, max(3, args.steps // 4), 2, layout, warm_s=0.3, min_timed_s=0.05)
             f = bwd_flops(xx)
             key = (f"{nm}_n{n}" if n else nm) + ("_bhsd" if layout == "bhsd" else "")
             extra[key] = {"bwd_tflops": round(f / ((rr["pre_ms"] + rr["bwd_ms"] + rr["post_ms"])
@@ -478,7 +508,7 @@ def main(argv=None) -> int:
                           "frac": round(f / (rr["bwd_ms"] * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
                           "atomic_gbs": round(bwd_atomic_bytes(xx) / (rr["bwd_ms"] * 1e-3) / 1e9, 1),
                           "fwd_tflops": round(fwd_flops(xx) / (rr["fwd_ms"] * 1e-3) / 1e12, 2),
-                          "attn_fwd_ms": round(rr["fwd_ms"], 4)}
+                          "attn_fwd_ms": round(rr["fwd_ms"], 4), "timed_steps": rr["steps"]}
             extra[key]["deterministic"] = deterministic_entry(xx, rr)
             extra[key]["auto"] = auto_entry(xx, rr)
             if xx["window"] > 0:
