@@ -8,9 +8,12 @@ postprocess) with no host synchronisation in between.
 ``backward`` has two orientations for dQ:
   * ``mode="atomic"`` (default): the key/value-stationary main pass sends dQ
     through region-wide fp32 atomics into an accumulator, cast afterwards;
-  * ``mode="deterministic"``: the same pass without its dQ product, then a
+  * ``mode="deterministic"``: the same pass without its dQ product, and a
     query-stationary dQ pass that keeps dQ on chip (no atomics, no
-    accumulator; every output bitwise reproducible);
+    accumulator; every output bitwise reproducible).  The two passes are
+    independent; where the first has a long tail (``concurrent_dq``) the dQ
+    pass runs on a second stream (default priority), forked after the
+    preprocess and joined before ``backward`` returns;
   * ``mode="auto"``: whichever of the two ``select_mode`` expects to be faster
     for the shape (measured crossover on MI355X, see ``select_mode``).
 """
@@ -124,20 +127,20 @@ def keys_per_query(shape: Shape, lengths=None) -> float:
 
 def select_mode(shape: Shape, lengths=None) -> str:
     """"deterministic" (query-stationary dQ) or "atomic", whichever measured
-    faster on MI355X for this kind of shape.  Backward times of both paths
-    (preprocess through dQ, deterministic / atomic), one MI355X:
-      D = 128: query-stationary faster up to ~1k keys per query (0.80x at
-      512, 0.87x at 1024, 1.03x at 2048, 1.11x at 4096) and with every window
-      measured (W = 128 .. 2048: 0.72x - 0.96x); the ragged varlen batch
-      (~1.2k keys per query) runs faster with atomics once its key blocks are
-      ranked longest first and split;
-      D = 64: atomic faster without a window (1.22x at 512 keys per query,
-      1.06x at 1024, 1.05x at 2048); with a window query-stationary is
-      faster up to the largest measured, W = 2048 (0.81x at 128, 0.88x at
-      512, 0.94x at 2048)."""
+    faster on MI355X for this kind of shape, each with its own split choice
+    and the deterministic dQ pass concurrent with the dK / dV pass (whole
+    backward, one MI355X, best split count of each):
+      D = 128: query-stationary faster up to ~1.5k keys per query (GQA 32/8,
+      4 x 1k: 0.19 vs 0.23 ms; 4 x 2k: 0.55 vs 0.60; the ragged varlen batch,
+      ~1.2k keys per query: 1.06 vs 1.13) and with every window measured
+      (W = 128 .. 2048); atomic faster from 2k keys per query (4 x 4k: 1.94
+      vs 2.00 ms; one 8k sequence: 1.81 vs 1.94; 32k: 53.6 vs 59.9);
+      D = 64: atomic faster without a window (4 x 2k: 0.102 vs 0.105 ms,
+      4 x 4k: 0.25 vs 0.31, 4 x 16k: 3.44 vs 4.05); with a window
+      query-stationary is faster up to the largest measured, W = 2048."""
     kq = keys_per_query(shape, lengths)
     if shape.head_dim == 128:
-        return "deterministic" if (shape.window > 0 or kq <= 1024) else "atomic"
+        return "deterministic" if (shape.window > 0 or kq <= 1536) else "atomic"
     return "deterministic" if 0 < shape.window <= 2048 else "atomic"
 
 
@@ -189,11 +192,48 @@ def select_splits(shape: Shape, lengths=None) -> int:
     return int(min(MAX_SPLIT, -(-longest // max(per_cu, 1.0))))
 
 
+def concurrent_dq(shape: Shape, lengths=None) -> bool:
+    """Whether the deterministic backward runs its dQ pass on a second stream,
+    concurrent with the dK / dV pass: where the dK / dV pass has a long tail
+    (its longest key block holds clearly more than a CU's share of the work,
+    the condition under which select_splits splits, or a window).  Measured
+    on MI355X, back to back -> concurrent: the varlen batch 1.21 -> 1.07 ms,
+    D=64 MHA 4 x 2k 0.119 -> 0.105 ms, the window problem 0.391 -> 0.381 ms;
+    where each pass fills the GPU alone it was slower (4 x 4k 0.29 -> 0.31
+    ms, 4 x 32k 15.6 -> 16.8 ms)."""
+    return shape.window > 0 or select_splits(shape, lengths) > 1
+
+
+def splits_for_mode(shape: Shape, lengths, mode: str) -> int:
+    """select_splits for the atomic backward; for the deterministic one,
+    half of it (rounded up), and none below three parts: its unsplit
+    dK / dV-only pass already runs 128-key workgroups, twice as many as the
+    256-key split pass has per part (measured: the varlen batch 1.06 ms
+    unsplit vs 1.16 ms in two parts; GQA 32/8 4 x 1k 0.19 ms in two parts vs
+    0.23 ms in four)."""
+    n = select_splits(shape, lengths)
+    if mode == "deterministic":
+        return 1 if n <= 2 else -(-n // 2)
+    return n
+
+
 def _split_workspace(inp: Inputs, ws: Workspace, nsplit: int) -> torch.Tensor:
     want = dkv_partial_shape(inp.shape, nsplit)
     if ws.dkv_part is None or tuple(ws.dkv_part.shape) != want:
         ws.dkv_part = torch.empty(want, device=inp.q.device, dtype=torch.float32)
     return ws.dkv_part
+
+
+_SIDE: dict = {}
+
+
+def _side_stream(device) -> torch.cuda.Stream:
+    """One extra stream per device (default priority) for the dQ pass of the
+    deterministic backward."""
+    key = torch.device(device).index
+    if key not in _SIDE:
+        _SIDE[key] = torch.cuda.Stream(device=device)
+    return _SIDE[key]
 
 
 def forward(inp: Inputs, ws: Workspace, stream=None) -> None:
@@ -203,9 +243,12 @@ def forward(inp: Inputs, ws: Workspace, stream=None) -> None:
 def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
              mode: str = "atomic", kv_splits=1) -> str:
     """Preprocess -> main backward -> postprocess; O and lse default to ws.o / ws.lse.
-    mode "deterministic": dK/dV pass + query-stationary dQ pass, no atomics
-    (ws.dq_accum unused); "auto": select_mode.  kv_splits > 1 (or "auto":
-    select_splits) splits every key block's pairs over that many workgroups,
+    mode "deterministic": dK/dV pass + query-stationary dQ pass (the latter on
+    a side stream where concurrent_dq says so, joined before returning), no
+    atomics (ws.dq_accum unused);
+    "auto": select_mode.  kv_splits > 1 (or "auto": select_splits, halved
+    for the deterministic mode) splits every key block's pairs over that many
+    workgroups,
     whose fp32 dK / dV partials are then summed in a fixed order
     (attn_bwd_split + attn_bwd_dkv_reduce; the partials live in ws.dkv_part,
     allocated on first use).  Returns the mode that ran."""
@@ -214,7 +257,7 @@ def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
     if mode not in ("atomic", "deterministic"):
         raise ValueError(f"unknown backward mode {mode!r}")
     if kv_splits == "auto":
-        kv_splits = select_splits(inp.shape, inp.lengths)
+        kv_splits = splits_for_mode(inp.shape, inp.lengths, mode)
     kv_splits = int(kv_splits)
     if not 1 <= kv_splits <= MAX_SPLIT:
         raise ValueError(f"kv_splits must be in [1, {MAX_SPLIT}] (got {kv_splits})")
@@ -223,6 +266,15 @@ def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
     det = mode == "deterministic"
     attn_bwd_preprocess(inp.shape, o, inp.do, lse, inp.cu, inp.sink, ws.delta,
                         None if det else ws.dq_accum, ws.dsink, stream)
+    conc = det and concurrent_dq(inp.shape, inp.lengths)
+    if conc:
+        # dQ pass on the side stream, concurrent with the dK / dV pass
+        # (both only read what the preprocess wrote; joined below).
+        main = torch.cuda.current_stream() if stream is None else stream
+        side = _side_stream(inp.q.device)
+        side.wait_stream(main)
+        attn_bwd_dq(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dq,
+                    side)
     if kv_splits > 1:
         part = _split_workspace(inp, ws, kv_splits)
         attn_bwd_split(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu,
@@ -232,9 +284,11 @@ def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
         attn_bwd_dkdv(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dk,
                       ws.dv, stream)
     else:
-        attn_bwd(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dq_accum,
-                 ws.dk, ws.dv, stream)
-    if det:
+        attn_bwd(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu,
+                 ws.dq_accum, ws.dk, ws.dv, stream)
+    if conc:
+        main.wait_stream(side)
+    elif det:
         attn_bwd_dq(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dq,
                     stream)
     else:

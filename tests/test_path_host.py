@@ -39,14 +39,17 @@ def test_keys_per_query_without_lengths_assumes_a_dense_batch():
     ("mha_causal", dict(n=32768), "atomic"),       # D=64 dense causal
     ("mha_causal", dict(n=1024), "atomic"),
     ("long_gqa", {}, "atomic"),                    # D=128, 16k keys per query
-    ("varlen_gqa", {}, "atomic"),                  # D=128, ~1.2k keys per query
+    ("varlen_gqa", {}, "deterministic"),           # D=128, ~1.2k keys per query
+    ("varlen_gqa", dict(seqlens=(4096,) * 4, draw_lengths=None), "atomic"),  # 2k keys per query
     ("sink_window", {}, "deterministic"),          # D=128, W=128
     ("mha_causal", dict(n=8192, window=128), "deterministic"),
     ("mha_causal", dict(n=8192, window=2048), "deterministic"),
     ("mha_causal", dict(n=8192, window=4096), "atomic"),
 ])
 def test_select_mode_follows_the_measured_crossover(name, kw, mode):
-    w = ai.workload(name, **kw)
+    w = ai.workload(name, **{k: v for k, v in kw.items() if k not in ("seqlens", "draw_lengths")})
+    if "seqlens" in kw:
+        w = w.with_(seqlens=kw["seqlens"], draw_lengths=kw["draw_lengths"])
     if w.draw_lengths is not None:  # the lengths generate() draws first with seed 0
         nseq, lo, hi = w.draw_lengths
         lengths = [int(x) for x in np.random.default_rng(0).integers(lo, hi + 1, nseq)]
@@ -118,3 +121,29 @@ def test_bad_split_count_is_rejected_before_any_launch():
         path.backward(inp, None, kv_splits=0)
     with pytest.raises(ValueError):
         path.backward(inp, None, kv_splits=17)
+
+
+@pytest.mark.parametrize("lengths,hq,hkv,d,atomic_parts", [
+    ([3561, 2795, 2344, 1479, 1615, 658, 781, 571], 32, 8, 128, 2),  # the varlen batch
+    ([1024] * 4, 32, 8, 128, 4),
+    ([32768] * 4, 8, 8, 64, 1),
+])
+def test_deterministic_mode_halves_the_split(lengths, hq, hkv, d, atomic_parts):
+    s = path.make_shape(lengths, hq, hkv, d, "bf16", True, 0, 0.1)
+    n = path.select_splits(s, lengths)
+    assert n == atomic_parts
+    assert path.splits_for_mode(s, lengths, "atomic") == n
+    det = path.splits_for_mode(s, lengths, "deterministic")
+    assert det == (1 if n <= 2 else -(-n // 2))
+
+
+@pytest.mark.parametrize("lengths,hq,hkv,d,window,conc", [
+    ([3561, 2795, 2344, 1479, 1615, 658, 781, 571], 32, 8, 128, 0, True),  # ragged: long tail
+    ([2048] * 4, 8, 8, 64, 0, True),       # 256 key blocks, longest 1.8x a CU's share
+    ([4096] * 2, 64, 8, 128, 128, True),   # window
+    ([4096] * 4, 8, 8, 64, 0, False),      # each pass fills the GPU alone
+    ([32768] * 4, 8, 8, 64, 0, False),
+])
+def test_concurrent_dq_where_the_dkdv_pass_has_a_tail(lengths, hq, hkv, d, window, conc):
+    s = path.make_shape(lengths, hq, hkv, d, "f16", True, window, 0.1)
+    assert path.concurrent_dq(s, lengths) == conc
