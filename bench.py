@@ -177,6 +177,18 @@ def prepost_bytes(x: dict) -> tuple:
     return pre, post
 
 
+def compulsory_bytes(x: dict) -> float:
+    """HBM bytes any backward must move at least once: read Q, K, V, O, dO
+    (storage dtype) and lse; write dQ, dK, dV (storage dtype) and Delta.
+    Their time at the HBM peak is the floor of the whole backward, whatever
+    the orientation (the MFMA floor is the other one)."""
+    T = float(sum(x["lengths"]))
+    d, e = x["d"], 2.0
+    q_side = T * x["hq"] * d * e  # one of Q, O, dO, dQ
+    kv_side = T * x["hkv"] * d * e  # one of K, V, dK, dV
+    return 4 * q_side + 4 * kv_side + 2 * 4 * T * x["hq"]
+
+
 def _code_only(text: str) -> str:
     """C++ source without comments and blank lines (string literals in these
     files hold no comment markers)."""
@@ -527,6 +539,11 @@ def main(argv=None) -> int:
                           "attn_fwd_ms": round(rr["fwd_ms"], 4), "timed_steps": rr["steps"]}
             extra[key]["deterministic"] = deterministic_entry(xx, rr)
             extra[key]["auto"] = auto_entry(xx, rr)
+            cb = compulsory_bytes(xx)
+            extra[key]["hbm_floor"] = {
+                "compulsory_bytes": cb, "floor_ms": round(cb / (PEAK_HBM_GBS * 1e9) * 1e3, 4),
+                "auto_gbs": round(cb / (rr["auto_ms"] * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(cb / (rr["auto_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
             if xx["window"] > 0:
                 extra[key]["attn_bwd_kernel_tflops_nominal_formula"] = round(
                     bwd_flops_nominal(xx) / (rr["bwd_ms"] * 1e-3) / 1e12, 2)

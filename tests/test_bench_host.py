@@ -96,3 +96,13 @@ def test_cpu_baseline_covers_the_workload_when_given_time():
     r = bench.cpu_baseline(ai.generate(w, 0), min_run_s=1e9)
     assert r["kind"] == "oracle" and r["value"] > 0
     assert f"length {w.seqlens[0]} x {w.hq} query head(s) / {w.hkv} kv head(s)" in r["sample"]
+
+
+def test_compulsory_bytes_of_the_window_workload():
+    import bench
+
+    x = dict(lengths=[4096, 4096], hq=64, hkv=8, d=128)
+    T = 8192
+    want = 4 * T * 64 * 128 * 2 + 4 * T * 8 * 128 * 2 + 8 * T * 64
+    assert bench.compulsory_bytes(x) == want
+    assert abs(want / 8e12 * 1e3 - 0.076) < 0.001  # ~76 us at 8 TB/s
