@@ -14,7 +14,7 @@ with the orientation path.select_mode picks for the shape, and the backward
 as path.backward(mode="auto", kv_splits="auto") runs it under "auto".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-       [--n N] [--seed S] [--no-cpu-baseline] [--no-extra]
+       [--n N] [--seed S] [--no-cpu-baseline] [--no-extra] [--only-extra KEY]
 """
 from __future__ import annotations
 
@@ -431,6 +431,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the per-workload extras (N sweep and GQA workloads)")
+    ap.add_argument("--only-extra", default=None, metavar="KEY",
+                    help="run only the per-workload extra with this key (e.g. mha_causal_n4096)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 launches) and exit: the "
                          "reference reading for the FETCH_SIZE / WRITE_SIZE counters")
@@ -524,11 +526,13 @@ def main(argv=None) -> int:
         if w.name == "mha_causal":  # the same dense batch as [B, H, S, D] tensors
             cases.append(("mha_causal", args.n, "bhsd"))
         for nm, n, layout in cases:
+            key = (f"{nm}_n{n}" if n else nm) + ("_bhsd" if layout == "bhsd" else "")
+            if args.only_extra is not None and key != args.only_extra:
+                continue
             wx = ai.workload(nm, n=n) if n else ai.workload(nm)
             xx = ai.generate(wx, args.seed)
             rr = run_gpu(xx, max(3, args.steps // 4), 2, layout, warm_s=0.3, min_timed_s=0.05)
             f = bwd_flops(xx)
-            key = (f"{nm}_n{n}" if n else nm) + ("_bhsd" if layout == "bhsd" else "")
             extra[key] = {"bwd_tflops": round(f / ((rr["pre_ms"] + rr["bwd_ms"] + rr["post_ms"])
                                                    * 1e-3) / 1e12, 2),
                           "attn_bwd_kernel_tflops": round(f / (rr["bwd_ms"] * 1e-3) / 1e12, 2),

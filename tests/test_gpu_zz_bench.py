@@ -39,5 +39,26 @@ def test_bench_line_contract(capsys):
     assert d["bwd_ms"] == pytest.approx(d["attn_bwd_preprocess_ms"] + d["attn_bwd_dkdv_ms"]
                                         + d["attn_bwd_dq_ms"], abs=2e-4)
     assert d["bwd_tflops"] > 0 and d["attn_bwd_dq_tflops"] > 0
+    # as path.backward runs it (dQ pass concurrent for windows)
+    assert d["bwd_ms_concurrent"] > 0
+    assert d["vs_atomic_path"] == pytest.approx(
+        (line["kernels_ms"]["attn_bwd_preprocess"] + line["kernels_ms"]["attn_bwd"]
+         + line["kernels_ms"]["attn_bwd_postprocess"]) / d["bwd_ms_concurrent"], rel=2e-3)
     au = line["auto"]
     assert au["mode"] == "deterministic" and au["kv_splits"] == 1 and au["bwd_tflops"] > 0
+
+
+def test_secondary_workloads_report_the_hbm_floor(capsys):
+    """A short sweep entry carries the compulsory-traffic floor and its timed
+    step count (warm-up for 0.3 s, then about 50 ms of timed steps)."""
+    rc = bench.main(["--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--n", "2048",
+                     "--only-extra", "mha_causal_n4096"])
+    assert rc == 0
+    line = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    e = line["per_workload"]["mha_causal_n4096"]
+    f = e["hbm_floor"]
+    x = dict(lengths=[4096] * 4, hq=8, hkv=8, d=64)
+    assert f["compulsory_bytes"] == bench.compulsory_bytes(x)
+    assert f["floor_ms"] == pytest.approx(f["compulsory_bytes"] / 8e12 * 1e3, rel=1e-3)
+    assert 0 < f["frac_of_peak"] < 1
+    assert e["timed_steps"] >= 3
