@@ -113,3 +113,37 @@ def test_concurrent_passes_equal_back_to_back(w):
         torch.cuda.synchronize()
         for n, t in ref.items():
             assert torch.equal(getattr(ws, n), t), n
+
+
+def test_concurrent_passes_on_a_caller_stream():
+    """The side stream forks from and joins back to the stream the caller
+    passes (not the default stream): results equal the default-stream run,
+    and work queued on the caller's stream after backward sees finished dQ."""
+    import torch
+
+    from atomics_bwd_preprocess_amd import path
+
+    w = ai.workload("varlen_gqa").with_(draw_lengths=None, seqlens=(1500, 333, 129, 64), hq=8,
+                                        hkv=2)
+    x = ai.generate(w, 12)
+    _announce(f"concurrent deterministic on a caller stream lengths={x['lengths']}")
+    inp = path.to_device(x)
+    assert path.concurrent_dq(inp.shape, inp.lengths)
+    ws = path.workspace(inp)
+    path.forward(inp, ws)
+    path.backward(inp, ws, mode="deterministic")
+    torch.cuda.synchronize()
+    ref = {n: getattr(ws, n).clone() for n in ("dq", "dk", "dv")}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(s):
+            for n in ref:
+                getattr(ws, n).fill_(5.0)
+            path.backward(inp, ws, stream=s, mode="deterministic")
+            dq_copy = ws.dq.clone()  # ordered after the join on s
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        assert torch.equal(dq_copy, ref["dq"])
+        for n, t in ref.items():
+            assert torch.equal(getattr(ws, n), t), n
