@@ -23,6 +23,7 @@ __all__ = [
     "attn_bwd_postprocess",
     "attn_bwd_dkdv",
     "attn_bwd_dq",
+    "attn_bwd_dsink",
     "attn_bwd_split",
     "attn_bwd_dkv_reduce",
     "MAX_SPLIT",
@@ -93,6 +94,7 @@ def lib() -> ctypes.CDLL:
             "attn_bwd_postprocess": [S, P, P, P],
             "attn_bwd_dkdv": [S, P, P, P, P, P, P, P, P, P, P],
             "attn_bwd_dq": [S, P, P, P, P, P, P, P, P, P],
+            "attn_bwd_dsink": [S, P, P, P, P, P],
             "attn_bwd_split": [S, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P],
             "attn_bwd_dkv_reduce": [S, P, ctypes.c_int32, P, P, P],
         }
@@ -286,6 +288,19 @@ def attn_bwd_dq(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dq, stream=
     _check(lib().attn_bwd_dq(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                              _ptr(lse), _ptr(delta), _cu(shape, cu_seqlens), _ptr(dq),
                              _stream(stream)))
+
+
+def attn_bwd_dsink(shape: Shape, lse, delta, sink, dsink, stream=None) -> None:
+    """dsink = -sum_t exp(sink - lse) * delta per query head (delta already written)."""
+    import torch
+
+    T, Hq, Hkv, D, dt = _dims(shape)
+    _need(lse, "lse", torch.float32, (Hq, T))
+    _need(delta, "delta", torch.float32, (Hq, T))
+    _need(sink, "sink", torch.float32, (Hq,))
+    _need(dsink, "dsink", torch.float32, (Hq,))
+    _check(lib().attn_bwd_dsink(ctypes.byref(shape), _ptr(lse), _ptr(delta), _ptr(sink),
+                                _ptr(dsink), _stream(stream)))
 
 
 def dkv_partial_shape(shape: Shape, nsplit: int) -> tuple:

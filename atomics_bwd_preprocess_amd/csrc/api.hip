@@ -143,6 +143,18 @@ attn_status_t attn_bwd_preprocess(const attn_shape_t* shape, const void* o, cons
                     "attn_bwd_preprocess");
 }
 
+attn_status_t attn_bwd_dsink(const attn_shape_t* shape, const float* lse, const float* delta,
+                             const float* sink, float* dsink, hipStream_t stream) {
+  attn::Problem p;
+  attn_status_t st = check_shape(shape, nullptr, false, p);
+  if (st != ATTN_OK) return st;
+  REQUIRE_F32(lse);
+  REQUIRE_F32(delta);
+  REQUIRE_F32(sink);
+  REQUIRE_F32(dsink);
+  return hip_status(attn::launch_dsink(p, lse, delta, sink, dsink, stream), "attn_bwd_dsink");
+}
+
 attn_status_t attn_bwd(const attn_shape_t* shape, const void* q, const void* k, const void* v,
                        const void* dout, const float* lse, const float* delta,
                        const int32_t* cu_seqlens, float* dq_accum, void* dk, void* dv,

@@ -34,6 +34,10 @@ hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void
                       const int32_t* cu, const float* sink, void* o, float* lse,
                       hipStream_t stream);
 
+// dsink only (Delta already written), fixed-order reduction per head.
+hipError_t launch_dsink(const Problem& p, const float* lse, const float* delta, const float* sink,
+                        float* dsink, hipStream_t stream);
+
 hipError_t launch_preprocess(const Problem& p, const void* o, const void* dout, const float* lse,
                              const float* sink, float* delta, float* dq_accum, float* dsink,
                              hipStream_t stream);

@@ -168,6 +168,13 @@ __global__ __launch_bounds__(256) void dkv_reduce_kernel(const float* __restrict
   }
 }
 
+hipError_t launch_dsink(const Problem& p, const float* lse, const float* delta, const float* sink,
+                        float* dsink, hipStream_t stream) {
+  hipLaunchKernelGGL(dsink_kernel, dim3(p.hq), dim3(kDsinkThreads), 0, stream, lse, delta, sink,
+                     dsink, p.total);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 static hipError_t preprocess_t(const Problem& p, const void* o, const void* dout,
                                const float* lse, const float* sink, float* delta,
@@ -189,9 +196,7 @@ static hipError_t preprocess_t(const Problem& p, const void* o, const void* dout
     if (e != hipSuccess) return e;
   }
   if (sink == nullptr) return hipSuccess;
-  hipLaunchKernelGGL(dsink_kernel, dim3(p.hq), dim3(kDsinkThreads), 0, stream, lse, delta, sink,
-                     dsink, p.total);
-  return hipGetLastError();
+  return launch_dsink(p, lse, delta, sink, dsink, stream);
 }
 
 hipError_t launch_preprocess(const Problem& p, const void* o, const void* dout, const float* lse,

@@ -25,6 +25,7 @@ from typing import Optional
 import torch
 
 from . import (MAX_SPLIT, Shape, attn_bwd, attn_bwd_dkdv, attn_bwd_dkv_reduce, attn_bwd_dq,
+               attn_bwd_dsink,
                attn_bwd_postprocess, attn_bwd_preprocess, attn_bwd_split, attn_fwd,
                dkv_partial_shape, kvshape, qshape)
 
@@ -264,9 +265,13 @@ def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
     o = ws.o if o is None else o
     lse = ws.lse if lse is None else lse
     det = mode == "deterministic"
-    attn_bwd_preprocess(inp.shape, o, inp.do, lse, inp.cu, inp.sink, ws.delta,
-                        None if det else ws.dq_accum, ws.dsink, stream)
     conc = det and concurrent_dq(inp.shape, inp.lengths)
+    # With the passes concurrent, dsink (which nothing else reads) is reduced
+    # after the dK / dV pass rather than ahead of both passes.
+    late_dsink = conc and inp.sink is not None
+    attn_bwd_preprocess(inp.shape, o, inp.do, lse, inp.cu, None if late_dsink else inp.sink,
+                        ws.delta, None if det else ws.dq_accum,
+                        None if late_dsink else ws.dsink, stream)
     if conc:
         # dQ pass on the side stream, concurrent with the dK / dV pass
         # (both only read what the preprocess wrote; joined below).
@@ -286,6 +291,8 @@ def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
     else:
         attn_bwd(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu,
                  ws.dq_accum, ws.dk, ws.dv, stream)
+    if late_dsink:
+        attn_bwd_dsink(inp.shape, lse, ws.delta, inp.sink, ws.dsink, stream)
     if conc:
         main.wait_stream(side)
     elif det:

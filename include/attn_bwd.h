@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 #define ATTN_MAX_SPLIT 16 /* largest nsplit of attn_bwd_split */
 
 typedef enum {
@@ -126,6 +126,17 @@ attn_status_t attn_bwd_preprocess(const attn_shape_t* shape, const void* o, cons
                                   const float* lse, const int32_t* cu_seqlens,
                                   const float* sink, float* delta, float* dq_accum,
                                   float* dsink, hipStream_t stream);
+
+/*
+ * dsink alone ([ASC] Dsink kernel): dsink[h] = -sum_t exp(sink[h] - lse[h][t])
+ * * delta[h][t] over all T tokens, written (not accumulated), fixed reduction
+ * order.  The same values attn_bwd_preprocess writes when given sink and
+ * dsink.  For callers that run the preprocess without sink (Delta only) and
+ * the reduction later, off the path of the main passes; it needs delta
+ * complete.
+ */
+attn_status_t attn_bwd_dsink(const attn_shape_t* shape, const float* lse, const float* delta,
+                             const float* sink, float* dsink, hipStream_t stream);
 
 /*
  * Backward main pass.  Recomputes S = Q K^T and P = exp(S*scale - lse) per

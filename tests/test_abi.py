@@ -27,7 +27,7 @@ def _declared():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["attn_fwd", "attn_bwd_preprocess", "attn_bwd",
                                   "attn_bwd_postprocess", "attn_bwd_dkdv", "attn_bwd_dq",
-                                  "attn_bwd_split", "attn_bwd_dkv_reduce",
+                                  "attn_bwd_split", "attn_bwd_dkv_reduce", "attn_bwd_dsink",
                                   "attn_status_string", "attn_last_error",
                                   "attn_abi_version"])
 
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     L = ab.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert ab.attn_abi_version() == 4
+    assert ab.attn_abi_version() == 5
     assert ab.MAX_SPLIT == int(re.search(r"#define ATTN_MAX_SPLIT (\d+)", open(HEADER).read()).group(1))
     assert L.attn_status_string(0) == b"ok"
     assert L.attn_status_string(1) == b"invalid argument"
@@ -174,3 +174,12 @@ def test_python_binding_rejects_host_tensors():
     q = torch.zeros(128, 4, 64, dtype=torch.float16)
     with pytest.raises(ab.AttnError):
         ab.attn_bwd_postprocess(s, torch.zeros(128, 4, 64), q)
+
+
+def test_dsink_rejects_bad_pointers_before_any_launch():
+    L, s = ab.lib(), _shape()
+    assert L.attn_bwd_dsink(ctypes.byref(s), None, FAKE, FAKE, FAKE, None) == 1
+    assert b"lse" in L.attn_last_error()
+    assert L.attn_bwd_dsink(ctypes.byref(s), FAKE, FAKE, None, FAKE, None) == 1
+    assert L.attn_bwd_dsink(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE + 2, None) == 1
+    assert L.attn_bwd_dsink(ctypes.byref(_shape(hq=3, hkv=2)), FAKE, FAKE, FAKE, FAKE, None) == 1
