@@ -121,14 +121,20 @@ def test_backward_alone_from_oracle_forward():
         assert_close(got[n], ref[n], n, w.dtype)
 
 
-def test_repeatability():
-    """dK / dV are written once from registers: bitwise identical run to run.
-    dQ and dsink only within tolerance (atomic order varies)."""
+@pytest.mark.parametrize("w", [
+    ai.workload("varlen_gqa").with_(draw_lengths=None, seqlens=(700, 333), hq=8, hkv=2),
+    ai.workload("mha_causal").with_(seqlens=(1000, 517), hq=4, hkv=4),
+    ai.workload("sink_window").with_(seqlens=(600, 200), hq=8, hkv=2, window=96),
+], ids=["varlen_d128", "causal_d64", "window_sink_d128"])
+def test_repeatability(w):
+    """30 runs ([ASC] tests its kernels over 30 cold-start runs): dK / dV are
+    written once from registers, so they are bitwise identical run to run;
+    dQ and dsink only within tolerance (atomic order varies).  The outputs
+    are overwritten with garbage between runs, so every run writes them."""
     import torch
 
-    w = ai.workload("varlen_gqa").with_(draw_lengths=None, seqlens=(700, 333), hq=8, hkv=2)
     x = ai.generate(w, 3)
-    _announce("repeatability x5")
+    _announce(f"repeatability x30 {w.name} lengths={x['lengths']}")
     from atomics_bwd_preprocess_amd import path
 
     inp = path.to_device(x)
@@ -136,7 +142,9 @@ def test_repeatability():
     path.step(inp, ws)
     torch.cuda.synchronize()
     dk0, dv0, dq0 = ws.dk.clone(), ws.dv.clone(), to64(ws.dq)
-    for _ in range(4):
+    for _ in range(29):
+        for t in (ws.dk, ws.dv, ws.dq):
+            t.fill_(float("nan"))
         path.step(inp, ws)
         torch.cuda.synchronize()
         assert torch.equal(ws.dk, dk0) and torch.equal(ws.dv, dv0)
