@@ -244,15 +244,15 @@ def forward(inp: Inputs, ws: Workspace, stream=None) -> None:
 def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
              mode: str = "atomic", kv_splits=1) -> str:
     """Preprocess -> main backward -> postprocess; O and lse default to ws.o / ws.lse.
-    mode "deterministic": dK/dV pass + query-stationary dQ pass (the latter on
-    a side stream where concurrent_dq says so, joined before returning), no
-    atomics (ws.dq_accum unused);
-    "auto": select_mode.  kv_splits > 1 (or "auto": select_splits, halved
-    for the deterministic mode) splits every key block's pairs over that many
-    workgroups,
-    whose fp32 dK / dV partials are then summed in a fixed order
-    (attn_bwd_split + attn_bwd_dkv_reduce; the partials live in ws.dkv_part,
-    allocated on first use).  Returns the mode that ran."""
+
+    mode "deterministic": dK/dV pass + query-stationary dQ pass, no atomics
+    (ws.dq_accum unused); where concurrent_dq says so, the dQ pass runs on a
+    side stream, joined before returning, and dsink is reduced after the dK/dV
+    pass.  "auto": select_mode.  kv_splits > 1 (or "auto": splits_for_mode)
+    splits every key block's pairs over that many workgroups, whose fp32
+    dK / dV partials are then summed in a fixed order (attn_bwd_split +
+    attn_bwd_dkv_reduce; the partials live in ws.dkv_part, allocated on first
+    use).  Returns the mode that ran."""
     if mode == "auto":
         mode = select_mode(inp.shape, inp.lengths)
     if mode not in ("atomic", "deterministic"):
