@@ -24,6 +24,7 @@ __all__ = [
     "attn_bwd_dkdv",
     "attn_bwd_dq",
     "attn_bwd_dsink",
+    "attn_bwd_dq_delta",
     "attn_bwd_split",
     "attn_bwd_dkv_reduce",
     "MAX_SPLIT",
@@ -95,6 +96,7 @@ def lib() -> ctypes.CDLL:
             "attn_bwd_dkdv": [S, P, P, P, P, P, P, P, P, P, P],
             "attn_bwd_dq": [S, P, P, P, P, P, P, P, P, P],
             "attn_bwd_dsink": [S, P, P, P, P, P],
+            "attn_bwd_dq_delta": [S, P, P, P, P, P, P, P, P, P, P],
             "attn_bwd_split": [S, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P],
             "attn_bwd_dkv_reduce": [S, P, ctypes.c_int32, P, P, P],
         }
@@ -288,6 +290,26 @@ def attn_bwd_dq(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dq, stream=
     _check(lib().attn_bwd_dq(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                              _ptr(lse), _ptr(delta), _cu(shape, cu_seqlens), _ptr(dq),
                              _stream(stream)))
+
+
+def attn_bwd_dq_delta(shape: Shape, q, k, v, o, dout, lse, cu_seqlens, delta, dq,
+                      stream=None) -> None:
+    """Query-stationary dQ that also forms Delta from O and dO (written to delta),
+    bitwise as attn_bwd_preprocess does; no preprocess needed before it."""
+    import torch
+
+    T, Hq, Hkv, D, dt = _dims(shape)
+    _need(q, "q", dt, qshape(shape))
+    _need(k, "k", dt, kvshape(shape))
+    _need(v, "v", dt, kvshape(shape))
+    _need(o, "o", dt, qshape(shape))
+    _need(dout, "dout", dt, qshape(shape))
+    _need(lse, "lse", torch.float32, (Hq, T))
+    _need(delta, "delta", torch.float32, (Hq, T))
+    _need(dq, "dq", dt, qshape(shape))
+    _check(lib().attn_bwd_dq_delta(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                   _ptr(dout), _ptr(lse), _cu(shape, cu_seqlens), _ptr(delta),
+                                   _ptr(dq), _stream(stream)))
 
 
 def attn_bwd_dsink(shape: Shape, lse, delta, sink, dsink, stream=None) -> None:

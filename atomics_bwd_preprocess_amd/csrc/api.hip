@@ -211,8 +211,30 @@ attn_status_t attn_bwd_dq(const attn_shape_t* shape, const void* q, const void* 
   REQUIRE_F32(delta);
   REQUIRE_TENSOR(dq);
   if (p.total == 0) return ok();
-  return hip_status(attn::launch_bwd_dq(p, q, k, v, dout, lse, delta, cu_seqlens, dq, stream),
+  return hip_status(attn::launch_bwd_dq(p, q, k, v, dout, lse, delta, cu_seqlens, dq, nullptr,
+                                        nullptr, stream),
                     "attn_bwd_dq");
+}
+
+attn_status_t attn_bwd_dq_delta(const attn_shape_t* shape, const void* q, const void* k,
+                                const void* v, const void* o, const void* dout, const float* lse,
+                                const int32_t* cu_seqlens, float* delta, void* dq,
+                                hipStream_t stream) {
+  attn::Problem p;
+  attn_status_t st = check_shape(shape, cu_seqlens, true, p);
+  if (st != ATTN_OK) return st;
+  REQUIRE_TENSOR(q);
+  REQUIRE_TENSOR(k);
+  REQUIRE_TENSOR(v);
+  REQUIRE_TENSOR(o);
+  REQUIRE_TENSOR(dout);
+  REQUIRE_F32(lse);
+  REQUIRE_F32(delta);
+  REQUIRE_TENSOR(dq);
+  if (p.total == 0) return ok();
+  return hip_status(attn::launch_bwd_dq(p, q, k, v, dout, lse, delta, cu_seqlens, dq, o, delta,
+                                        stream),
+                    "attn_bwd_dq_delta");
 }
 
 attn_status_t attn_bwd_split(const attn_shape_t* shape, const void* q, const void* k,

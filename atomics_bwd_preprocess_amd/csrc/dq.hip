@@ -25,6 +25,7 @@
 // Waves skip blocks that are hidden from all of their rows; masks are applied
 // only on blocks that need them; one workgroup barrier per block.
 #include "common.h"
+#include "delta_dot.h"
 #include "launch.h"
 
 namespace attn {
@@ -56,6 +57,10 @@ struct DqArgs {
   const float* delta;
   const int32_t* cu;
   void* dq;
+  // Optional: O, to form Delta here instead of reading it (written to
+  // delta_out), in the preprocess's arithmetic and summation order.
+  const void* o;
+  float* delta_out;
   int num_seqs, max_seqlen, total, hq, hkv, window, nqb;
   bool causal;
   float scale, scale_log2;
@@ -109,7 +114,36 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(DqArgs p) {
     dreg[ks] = __builtin_bit_cast(T8, buf_load16(dr, off));
   }
   float l2 = INFINITY, dlt = 0.0f;  // lse * log2(e) and Delta of query qi
-  if (qi < L) {
+  if (p.o) {
+    // Delta of this lane's row from O and dO, bit for bit as the preprocess
+    // forms it: dot8 per 8-element chunk, then the chunks summed in its
+    // butterfly order.  Chunk j of the row sits in lane c = j % 2, slot
+    // ks = j / 2, so the butterfly steps over chunk distances D/16 .. 2 stay
+    // inside the lane (slot distance D/32 .. 1) and the last one, distance 1,
+    // pairs the two lanes (xor 32).
+    const rsrc_t orr = make_rsrc(static_cast<const T*>(p.o) + qbase, qrows * q_row * 2);
+    float v[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const uint32_t off = ((32 * w + n) * q_row + 16 * ks + 8 * c) * 2;
+      v[ks] = dot8(__builtin_bit_cast(T8, buf_load16(orr, off)), dreg[ks], 0.0f);
+    }
+#pragma unroll
+    for (int hs = D / 32; hs >= 1; hs >>= 1) {
+      float u[D / 16];
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) u[ks] = v[ks] + v[ks ^ hs];
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) v[ks] = u[ks];
+    }
+    const float dfull = v[0] + xor32(v[0]);
+    if (qi < L) {
+      const size_t idx = (size_t)h * p.total + a + qi;
+      l2 = p.lse[idx] * kLog2e;
+      dlt = dfull;
+      if (c == 0) p.delta_out[idx] = dfull;
+    }
+  } else if (qi < L) {
     const size_t idx = (size_t)h * p.total + a + qi;
     l2 = p.lse[idx] * kLog2e;
     dlt = p.delta[idx];
@@ -268,7 +302,8 @@ hipError_t dq_t(const DqArgs& args, bool bhsd, hipStream_t stream) {
 
 hipError_t launch_bwd_dq(const Problem& p, const void* q, const void* k, const void* v,
                          const void* dout, const float* lse, const float* delta,
-                         const int32_t* cu, void* dq, hipStream_t stream) {
+                         const int32_t* cu, void* dq, const void* o, float* delta_out,
+                         hipStream_t stream) {
   DqArgs a;
   a.q = q;
   a.k = k;
@@ -278,6 +313,8 @@ hipError_t launch_bwd_dq(const Problem& p, const void* q, const void* k, const v
   a.delta = delta;
   a.cu = cu;
   a.dq = dq;
+  a.o = o;
+  a.delta_out = delta_out;
   a.num_seqs = p.num_seqs;
   a.max_seqlen = p.max_seqlen;
   a.total = p.total;

@@ -52,10 +52,13 @@ hipError_t launch_bwd_dkdv(const Problem& p, const void* q, const void* k, const
                            const void* dout, const float* lse, const float* delta,
                            const int32_t* cu, void* dk, void* dv, hipStream_t stream);
 
-// Query-stationary dQ pass (dQ written once in the storage dtype).
+// Query-stationary dQ pass (dQ written once in the storage dtype).  With o
+// non-null it forms Delta from O and dO itself (written to delta_out) instead
+// of reading delta.
 hipError_t launch_bwd_dq(const Problem& p, const void* q, const void* k, const void* v,
                          const void* dout, const float* lse, const float* delta,
-                         const int32_t* cu, void* dq, hipStream_t stream);
+                         const int32_t* cu, void* dq, const void* o, float* delta_out,
+                         hipStream_t stream);
 
 // Main pass with the pairs of every key block split over nsplit workgroups;
 // fp32 dK / dV partials into dkv_part (no dQ product when dq_accum is NULL).

@@ -15,35 +15,10 @@
 //   dsink kernel:  R * 8 (lse, Delta)
 //   postprocess:   R * D * (4 + e)
 #include "common.h"
+#include "delta_dot.h"
 #include "launch.h"
 
 namespace attn {
-
-// acc + a . b over 8 elements, two per v_dot2_f32_{f16,bf16} (exact 16-bit
-// products, fp32 accumulation), in a fixed order.  Written with the dot2
-// builtins rather than as `acc += a[i] * b[i]` so that every instantiation
-// of the delta kernel (with or without zeroing the accumulator) computes Delta
-// with the same instructions: left to the compiler, the loop was lowered to
-// dot2 in one build and to FMA chains in another, and the two backward paths
-// read Delta from different instantiations (dK / dV must agree bit for bit).
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float dot8(f16x8 a, f16x8 b, float acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2_t x = {a[2 * i], a[2 * i + 1]}, y = {b[2 * i], b[2 * i + 1]};
-    acc = __builtin_amdgcn_fdot2(x, y, acc, false);
-  }
-  return acc;
-}
-__device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b, float acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16x2_t x = {a[2 * i], a[2 * i + 1]}, y = {b[2 * i], b[2 * i + 1]};
-    acc = __builtin_amdgcn_fdot2_f32_bf16(x, y, acc, false);
-  }
-  return acc;
-}
 
 // One workgroup: query head blockIdx.y, tokens [blockIdx.x * 64, +64).
 // A row (token, head) is D contiguous elements read as 16-byte chunks by

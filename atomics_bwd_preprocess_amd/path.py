@@ -10,10 +10,11 @@ postprocess) with no host synchronisation in between.
     through region-wide fp32 atomics into an accumulator, cast afterwards;
   * ``mode="deterministic"``: the same pass without its dQ product, and a
     query-stationary dQ pass that keeps dQ on chip (no atomics, no
-    accumulator; every output bitwise reproducible).  The two passes are
-    independent; where the first has a long tail (``concurrent_dq``) the dQ
-    pass runs on a second stream (default priority), forked after the
-    preprocess and joined before ``backward`` returns;
+    accumulator; every output bitwise reproducible).  The dQ pass forms Delta
+    itself and runs first, or, where the dK / dV pass has a long tail
+    (``concurrent_dq``), the preprocess forms Delta and the dQ pass runs on a
+    second stream (default priority) beside the dK / dV pass, joined before
+    ``backward`` returns;
   * ``mode="auto"``: whichever of the two ``select_mode`` expects to be faster
     for the shape (measured crossover on MI355X, see ``select_mode``).
 """
@@ -25,7 +26,7 @@ from typing import Optional
 import torch
 
 from . import (MAX_SPLIT, Shape, attn_bwd, attn_bwd_dkdv, attn_bwd_dkv_reduce, attn_bwd_dq,
-               attn_bwd_dsink,
+               attn_bwd_dq_delta, attn_bwd_dsink,
                attn_bwd_postprocess, attn_bwd_preprocess, attn_bwd_split, attn_fwd,
                dkv_partial_shape, kvshape, qshape)
 
@@ -129,8 +130,8 @@ def keys_per_query(shape: Shape, lengths=None) -> float:
 def select_mode(shape: Shape, lengths=None) -> str:
     """"deterministic" (query-stationary dQ) or "atomic", whichever measured
     faster on MI355X for this kind of shape, each with its own split choice
-    and the deterministic dQ pass concurrent with the dK / dV pass (whole
-    backward, one MI355X, best split count of each):
+    and the deterministic passes ordered by concurrent_dq (whole backward, one
+    MI355X, best split count of each):
       D = 128: query-stationary faster up to ~1.5k keys per query (GQA 32/8,
       4 x 1k: 0.19 vs 0.23 ms; 4 x 2k: 0.55 vs 0.60; the ragged varlen batch,
       ~1.2k keys per query: 1.06 vs 1.13) and with every window measured
@@ -194,15 +195,21 @@ def select_splits(shape: Shape, lengths=None) -> int:
 
 
 def concurrent_dq(shape: Shape, lengths=None) -> bool:
-    """Whether the deterministic backward runs its dQ pass on a second stream,
-    concurrent with the dK / dV pass: where the dK / dV pass has a long tail
-    (its longest key block holds clearly more than a CU's share of the work,
-    the condition under which select_splits splits, or a window).  Measured
-    on MI355X, back to back -> concurrent: the varlen batch 1.21 -> 1.07 ms,
-    D=64 MHA 4 x 2k 0.119 -> 0.105 ms, the window problem 0.391 -> 0.381 ms;
-    where each pass fills the GPU alone it was slower (4 x 4k 0.29 -> 0.31
-    ms, 4 x 32k 15.6 -> 16.8 ms)."""
-    return shape.window > 0 or select_splits(shape, lengths) > 1
+    """How the deterministic backward orders its passes.  True: preprocess,
+    then the dQ pass on a second stream concurrent with the dK / dV pass --
+    where the dK / dV pass has a long tail (its longest key block holds
+    clearly more than a CU's share of the work, the condition under which
+    select_splits splits) and the dQ workgroups fill the CUs it leaves idle.
+    False: the dQ pass first, forming Delta itself (attn_bwd_dq_delta, no
+    preprocess), then the dK / dV pass.  Measured on MI355X:
+      long tail, back to back -> concurrent: the varlen batch 1.21 -> 1.07 ms
+      (0.121 -> 0.105 ms D=64 MHA 4 x 2k); the Delta-forming order there
+      1.21 ms;
+      otherwise (and for windows) concurrent -> Delta-forming order:
+      the window problem 0.375 -> 0.367 ms, 4 x 4k 0.291 -> 0.287 ms,
+      4 x 32k 15.45 -> 15.34 ms (concurrent was slower than back to back
+      there: 15.6 -> 16.8 ms)."""
+    return shape.window == 0 and select_splits(shape, lengths) > 1
 
 
 def splits_for_mode(shape: Shape, lengths, mode: str) -> int:
@@ -245,10 +252,11 @@ def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
              mode: str = "atomic", kv_splits=1) -> str:
     """Preprocess -> main backward -> postprocess; O and lse default to ws.o / ws.lse.
 
-    mode "deterministic": dK/dV pass + query-stationary dQ pass, no atomics
-    (ws.dq_accum unused); where concurrent_dq says so, the dQ pass runs on a
-    side stream, joined before returning, and dsink is reduced after the dK/dV
-    pass.  "auto": select_mode.  kv_splits > 1 (or "auto": splits_for_mode)
+    mode "deterministic": query-stationary dQ pass + dK/dV pass, no atomics
+    (ws.dq_accum unused), ordered as concurrent_dq says: the dQ pass forming
+    Delta first, or (long dK/dV tail) the preprocess and then the dQ pass on
+    a side stream beside the dK/dV pass, joined before returning; dsink is
+    reduced after the dK/dV pass.  "auto": select_mode.  kv_splits > 1 (or "auto": splits_for_mode)
     splits every key block's pairs over that many workgroups, whose fp32
     dK / dV partials are then summed in a fixed order (attn_bwd_split +
     attn_bwd_dkv_reduce; the partials live in ws.dkv_part, allocated on first
@@ -266,12 +274,17 @@ def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
     lse = ws.lse if lse is None else lse
     det = mode == "deterministic"
     conc = det and concurrent_dq(inp.shape, inp.lengths)
-    # With the passes concurrent, dsink (which nothing else reads) is reduced
-    # after the dK / dV pass rather than ahead of both passes.
-    late_dsink = conc and inp.sink is not None
-    attn_bwd_preprocess(inp.shape, o, inp.do, lse, inp.cu, None if late_dsink else inp.sink,
-                        ws.delta, None if det else ws.dq_accum,
-                        None if late_dsink else ws.dsink, stream)
+    if det and not conc:
+        # dQ pass first, forming Delta (bitwise as the preprocess would),
+        # then the dK / dV pass, then dsink.
+        attn_bwd_dq_delta(inp.shape, inp.q, inp.k, inp.v, o, inp.do, lse, inp.cu, ws.delta,
+                          ws.dq, stream)
+    else:
+        # With the passes concurrent, dsink (which nothing else reads) is
+        # reduced after the dK / dV pass rather than ahead of both passes.
+        attn_bwd_preprocess(inp.shape, o, inp.do, lse, inp.cu, None if det else inp.sink,
+                            ws.delta, None if det else ws.dq_accum,
+                            None if det else ws.dsink, stream)
     if conc:
         # dQ pass on the side stream, concurrent with the dK / dV pass
         # (both only read what the preprocess wrote; joined below).
@@ -291,14 +304,11 @@ def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
     else:
         attn_bwd(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu,
                  ws.dq_accum, ws.dk, ws.dv, stream)
-    if late_dsink:
+    if det and inp.sink is not None:
         attn_bwd_dsink(inp.shape, lse, ws.delta, inp.sink, ws.dsink, stream)
     if conc:
         main.wait_stream(side)
-    elif det:
-        attn_bwd_dq(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dq,
-                    stream)
-    else:
+    elif not det:
         attn_bwd_postprocess(inp.shape, ws.dq_accum, ws.dq, stream)
     return mode
 

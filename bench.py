@@ -297,8 +297,8 @@ def run_gpu(x: dict, steps: int, warmup: int, layout: str = "thd", warm_s: float
         e[3].record(stream)
     torch.cuda.synchronize()
     dm = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(3)] for e in ev]).mean(axis=0)
-    # ... and as path.backward runs it: the dQ pass on a side stream,
-    # concurrent with the dK/dV pass.
+    # ... and as path.backward runs it (path.concurrent_dq: the dQ pass
+    # forming Delta first, or on a side stream beside the dK/dV pass).
     _warm(lambda: path.backward(inp, ws, mode="deterministic"), 2, warm_s)
     for i in range(steps):
         ev[i][0].record(stream)
@@ -325,17 +325,18 @@ def run_gpu(x: dict, steps: int, warmup: int, layout: str = "thd", warm_s: float
 
 def deterministic_entry(x: dict, r: dict) -> dict:
     """Times and rates of the deterministic backward (query-stationary dQ):
-    per pass, back to back (bwd_ms), and as path.backward runs it, with the
-    dQ pass concurrent with the dK/dV pass (bwd_ms_concurrent; its ratio to
-    the atomic path is vs_atomic_path).  The dK/dV pass does 8 and the dQ
+    per pass, back to back after the preprocess (bwd_ms), and as
+    path.backward runs it (bwd_ms_path: the dQ pass forming Delta first, or
+    concurrent with the dK/dV pass; its ratio to the atomic path is
+    vs_atomic_path).  The dK/dV pass does 8 and the dQ
     pass 6 of the 10 units of 2*BM*BN*D FLOPs per visible tile pair that the
     fused pass does."""
     f = bwd_flops(x)
     total = r["det_pre_ms"] + r["dkdv_ms"] + r["dq_ms"]
     conc = r["det_path_ms"]
     return {"bwd_ms": round(total, 4), "bwd_tflops": round(f / (total * 1e-3) / 1e12, 2),
-            "bwd_ms_concurrent": round(conc, 4),
-            "bwd_tflops_concurrent": round(f / (conc * 1e-3) / 1e12, 2),
+            "bwd_ms_path": round(conc, 4),
+            "bwd_tflops_path": round(f / (conc * 1e-3) / 1e12, 2),
             "attn_bwd_preprocess_ms": round(r["det_pre_ms"], 4),
             "attn_bwd_dkdv_ms": round(r["dkdv_ms"], 4),
             "attn_bwd_dq_ms": round(r["dq_ms"], 4),

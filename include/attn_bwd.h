@@ -185,6 +185,23 @@ attn_status_t attn_bwd_dq(const attn_shape_t* shape, const void* q, const void* 
                           const int32_t* cu_seqlens, void* dq, hipStream_t stream);
 
 /*
+ * attn_bwd_dq that also forms Delta: [ASC]'s single-kernel revision folds
+ * the preprocess into its backward kernel as Phase 0; here the
+ * query-stationary dQ pass reads O beside dO and computes
+ *   delta[h][t] = sum_d o[t][h][d] * dout[t][h][d]
+ * for its own rows, writes it (every row of every sequence exactly once) and
+ * uses it.  The arithmetic and summation order are those of
+ * attn_bwd_preprocess, so delta is bitwise the same.  For a deterministic
+ * backward without the preprocess:
+ * attn_bwd_dq_delta, then attn_bwd_dkdv (which reads delta), then
+ * attn_bwd_dsink if there is a sink.  dq_accum is not used.
+ */
+attn_status_t attn_bwd_dq_delta(const attn_shape_t* shape, const void* q, const void* k,
+                                const void* v, const void* o, const void* dout, const float* lse,
+                                const int32_t* cu_seqlens, float* delta, void* dq,
+                                hipStream_t stream);
+
+/*
  * Main backward pass (as attn_bwd, or as attn_bwd_dkdv when dq_accum is NULL)
  * with the query loop of every key block split over `nsplit` workgroups
  * (1..ATTN_MAX_SPLIT), for problems whose longest key block sets the

@@ -28,6 +28,7 @@ def test_header_declares_the_boundary():
     assert _declared() == sorted(["attn_fwd", "attn_bwd_preprocess", "attn_bwd",
                                   "attn_bwd_postprocess", "attn_bwd_dkdv", "attn_bwd_dq",
                                   "attn_bwd_split", "attn_bwd_dkv_reduce", "attn_bwd_dsink",
+                                  "attn_bwd_dq_delta",
                                   "attn_status_string", "attn_last_error",
                                   "attn_abi_version"])
 
@@ -183,3 +184,17 @@ def test_dsink_rejects_bad_pointers_before_any_launch():
     assert L.attn_bwd_dsink(ctypes.byref(s), FAKE, FAKE, None, FAKE, None) == 1
     assert L.attn_bwd_dsink(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE + 2, None) == 1
     assert L.attn_bwd_dsink(ctypes.byref(_shape(hq=3, hkv=2)), FAKE, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_dq_delta_rejects_bad_pointers_before_any_launch():
+    L, s = ab.lib(), _shape()
+    args = [FAKE] * 9
+    for i, name in [(3, b"o"), (7, b"delta"), (8, b"dq")]:
+        bad = list(args)
+        bad[i] = None
+        assert L.attn_bwd_dq_delta(ctypes.byref(s), *bad, None) == 1
+        assert name in L.attn_last_error()
+    bad = list(args)
+    bad[3] = FAKE + 8  # o misaligned
+    assert L.attn_bwd_dq_delta(ctypes.byref(s), *bad, None) == 1
+    assert L.attn_bwd_dq_delta(ctypes.byref(_shape(head_dim=96)), *args, None) == 2

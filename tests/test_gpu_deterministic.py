@@ -79,23 +79,27 @@ def test_full_size_sampled(name):
     _sampled_compare(ai.workload(name), deterministic=True)
 
 
-@pytest.mark.parametrize("w", [
-    ai.workload("varlen_gqa").with_(draw_lengths=None, seqlens=(1500, 333, 129, 64), hq=8, hkv=2),
-    ai.workload("sink_window").with_(seqlens=(700, 300), hq=8, hkv=2, window=128),
-], ids=["ragged_d128", "window_sink_d128"])
-def test_concurrent_passes_equal_back_to_back(w):
-    """Where concurrent_dq holds, path.backward runs the dQ pass on a second
-    stream beside the dK / dV pass; the outputs must be bitwise those of the
-    two passes issued back to back on one stream, on every repeat."""
+@pytest.mark.parametrize("w,conc", [
+    (ai.workload("varlen_gqa").with_(draw_lengths=None, seqlens=(1500, 333, 129, 64), hq=8,
+                                     hkv=2), True),
+    (ai.workload("sink_window").with_(seqlens=(700, 300), hq=8, hkv=2, window=128), False),
+    (ai.workload("mha_causal").with_(seqlens=(4096,) * 4), False),  # no tail: fills the GPU
+], ids=["ragged_d128_concurrent", "window_sink_d128_delta_in_dq", "causal_d64_delta_in_dq"])
+def test_path_orders_equal_back_to_back(w, conc):
+    """path.backward orders the deterministic passes as concurrent_dq says:
+    the dQ pass on a second stream beside the dK / dV pass (long tail), or the
+    dQ pass first, forming Delta itself.  Either way every output (Delta
+    included) must be bitwise that of the preprocess and the two passes
+    issued back to back on one stream, on every repeat."""
     import torch
 
     import atomics_bwd_preprocess_amd as ab
     from atomics_bwd_preprocess_amd import path
 
     x = ai.generate(w, 11)
-    _announce(f"concurrent vs back-to-back deterministic {w.name} lengths={x['lengths']}")
+    _announce(f"deterministic path order vs back to back {w.name} lengths={x['lengths']}")
     inp = path.to_device(x)
-    assert path.concurrent_dq(inp.shape, inp.lengths)
+    assert path.concurrent_dq(inp.shape, inp.lengths) == conc
     ws = path.workspace(inp)
     path.forward(inp, ws)
     ab.attn_bwd_preprocess(inp.shape, ws.o, inp.do, ws.lse, inp.cu, inp.sink, ws.delta, None,
@@ -107,7 +111,7 @@ def test_concurrent_passes_equal_back_to_back(w):
     ref = {n: getattr(ws, n).clone() for n in ("delta", "dq", "dk", "dv", "dsink")
            if getattr(ws, n) is not None}
     for _ in range(3):
-        for n in ("dq", "dk", "dv"):
+        for n in ref:
             getattr(ws, n).fill_(7.0)
         assert path.backward(inp, ws, mode="deterministic") == "deterministic"
         torch.cuda.synchronize()

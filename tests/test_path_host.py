@@ -140,10 +140,10 @@ def test_deterministic_mode_halves_the_split(lengths, hq, hkv, d, atomic_parts):
 @pytest.mark.parametrize("lengths,hq,hkv,d,window,conc", [
     ([3561, 2795, 2344, 1479, 1615, 658, 781, 571], 32, 8, 128, 0, True),  # ragged: long tail
     ([2048] * 4, 8, 8, 64, 0, True),       # 256 key blocks, longest 1.8x a CU's share
-    ([4096] * 2, 64, 8, 128, 128, True),   # window
+    ([4096] * 2, 64, 8, 128, 128, False),  # window: the Delta-forming order
     ([4096] * 4, 8, 8, 64, 0, False),      # each pass fills the GPU alone
     ([32768] * 4, 8, 8, 64, 0, False),
 ])
-def test_concurrent_dq_where_the_dkdv_pass_has_a_tail(lengths, hq, hkv, d, window, conc):
+def test_concurrent_dq_only_where_the_dkdv_pass_has_a_tail(lengths, hq, hkv, d, window, conc):
     s = path.make_shape(lengths, hq, hkv, d, "f16", True, window, 0.1)
     assert path.concurrent_dq(s, lengths) == conc
