@@ -68,6 +68,13 @@ EDGE = [
     ("window_ge_len", ai.workload("sink_window").with_(seqlens=(150,), hq=4, hkv=2, window=400)),
     ("window_lt_bm", ai.workload("sink_window").with_(seqlens=(260,), hq=4, hkv=1, window=37,
                                                       sink=False)),
+    # D = 64 windows (64-row query tiles): narrower than a tile, and spanning
+    # several tiles and two key blocks, with a sink
+    ("d64_window_lt_bm_sink", ai.workload("mha_causal").with_(seqlens=(300, 90), hq=4, hkv=2,
+                                                              window=37, sink=True)),
+    ("d64_window_multi_tile", ai.workload("mha_causal").with_(seqlens=(600, 130), hq=4, hkv=1,
+                                                              window=200, sink=True,
+                                                              dtype="bf16")),
     ("d64_noncausal_sink", ai.workload("tiny_gqa").with_(seqlens=(190, 65), sink=True)),
     ("d128_noncausal_f16", ai.workload("tiny_gqa").with_(seqlens=(129,), d=128)),
     ("d64_bf16_causal", ai.workload("mha_causal").with_(seqlens=(255,), hq=4, hkv=4,
