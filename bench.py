@@ -353,65 +353,96 @@ def auto_entry(x: dict, r: dict) -> dict:
             "bwd_tflops": round(bwd_flops(x) / (r["auto_ms"] * 1e-3) / 1e12, 2)}
 
 
-def oracle_sample(x: dict, n_s: int, nh: int) -> dict:
-    """The sub-problem the CPU baseline times: the first n_s rows of the
-    packed batch as one sequence (the first sequence's rows when it is at
-    least n_s long), for query heads [0, nh) and the kv heads they read.
-    Query head h reads kv head h // G; below one group every head reads kv
-    head 0, and above it the sample keeps whole groups (nh rounded up), so
-    the oracle's own grouping (hq / hkv heads per kv head) is the
-    workload's."""
-    g = x["hq"] // x["hkv"]
-    if nh > g:
-        nh = min(x["hq"], -(-nh // g) * g)
-    nkv = -(-nh // g)
-    sub = dict(x)
-    sub["q"] = x["q"][:n_s, :nh]
-    sub["do"] = x["do"][:n_s, :nh]
-    sub["k"] = x["k"][:n_s, :nkv]
-    sub["v"] = x["v"][:n_s, :nkv]
-    sub["sink"] = None if x["sink"] is None else x["sink"][:nh]
-    sub["cu_seqlens"] = np.array([0, n_s], dtype=np.int32)
-    sub["lengths"] = [n_s]
-    sub["hq"], sub["hkv"] = nh, nkv
-    return sub
+def _oracle_unit(u: dict) -> float:
+    """One (sequence, query head) problem of the CPU baseline: the fp64 oracle's
+    forward + backward with one BLAS thread.  Returns its wall time."""
+    from threadpoolctl import threadpool_limits
 
-
-def cpu_baseline(x: dict, min_run_s: float = 10.0) -> dict:
-    """The fp64 oracle (as it stands) on a bounded sample of the workload:
-    the first sequence's first n_s rows for the first nh query heads (with
-    their kv heads), n_s doubled up to the workload's length and then nh
-    doubled, until one run takes >= min_run_s or covers the whole sequence
-    and every head."""
     from oracle import attention as orc
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = 1
-    n_max = max(x["lengths"])
-    n_s, nh = min(1024, n_max), 1
-    while True:
-        sub = oracle_sample(x, n_s, nh)
-        nh = sub["hq"]
+    with threadpool_limits(1):
         t0 = time.perf_counter()
-        orc.forward_backward(sub)
-        dt = time.perf_counter() - t0
-        if dt >= min_run_s or (n_s >= n_max and nh >= x["hq"]):
-            break
-        if n_s < n_max:
-            n_s = min(n_max, 2 * n_s)
-        else:
-            nh = min(x["hq"], 2 * nh)
-    flops = bwd_flops(sub)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": (f"fp64 numpy oracle forward+backward, 1 sequence of length {n_s} x "
-                       f"{sub['hq']} query head(s) / {sub['hkv']} kv head(s) (D={x['d']}, "
-                       f"causal={x['causal']}, window={x['window']}) taking {dt:.2f} s; rate = "
-                       f"backward FLOPs of that sample / its wall time")}
+        orc.forward_backward(u)
+        return time.perf_counter() - t0
+
+
+def oracle_units(x: dict, n_cap: int) -> list:
+    """Every (sequence, query head) of the workload as a problem of its own --
+    one sequence, one query head and the kv head it reads, its sink -- with
+    the sequence cut to its first n_cap rows; sequence-major, then head."""
+    g = x["hq"] // x["hkv"]
+    cu = x["cu_seqlens"]
+    out = []
+    for s in range(len(x["lengths"])):
+        a = int(cu[s])
+        n = min(int(cu[s + 1]) - a, n_cap)
+        if n <= 0:
+            continue
+        for h in range(x["hq"]):
+            kv = h // g
+            out.append(dict(q=x["q"][a:a + n, h:h + 1], k=x["k"][a:a + n, kv:kv + 1],
+                            v=x["v"][a:a + n, kv:kv + 1], do=x["do"][a:a + n, h:h + 1],
+                            sink=None if x["sink"] is None else x["sink"][h:h + 1],
+                            cu_seqlens=np.array([0, n], dtype=np.int32), lengths=[n], hq=1,
+                            hkv=1, d=x["d"], causal=x["causal"], window=x["window"],
+                            scale=x["scale"]))
+    return out
+
+
+def cpu_workers(cap: int = 16) -> tuple:
+    """(CPUs this process may run on, workers the CPU baseline uses): one
+    worker per CPU, at most `cap` (the host share of one GPU)."""
+    try:
+        cpus = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cpus = os.cpu_count() or 1
+    return cpus, max(1, min(cap, cpus))
+
+
+def cpu_baseline(x: dict, target_s: float = 12.0, workers: int | None = None) -> dict:
+    """The fp64 oracle (as it stands) on a bounded sample of the workload, in
+    a process pool over (sequence, query head) problems, one BLAS thread per
+    worker.  A 1024-row problem timed first sets the cost model (time ~ rows
+    squared); sequences are then cut to the longest prefix whose problem
+    takes about target_s or less, and whole rounds of `workers` problems
+    (sequence-major, then head) are taken until the pool's expected wall time
+    reaches target_s (or the workload is exhausted).  The rate is the sample's
+    backward FLOPs (same convention as the GPU figure) over the pool's wall
+    time.  Called before the GPU is touched: the pool's workers are started
+    fresh (spawn)."""
+    import multiprocessing as mp
+
+    cpus, nw = cpu_workers()
+    if workers is not None:
+        nw = workers
+    n_max = max(x["lengths"]) if x["lengths"] else 0
+    n_c = min(1024, n_max)
+    t_c = max(1e-3, _oracle_unit(oracle_units(x, n_c)[0]))
+    n_cap = n_max
+    while n_cap > n_c and t_c * (n_cap / n_c) ** 2 > target_s:
+        n_cap //= 2
+    units = oracle_units(x, n_cap)
+    cost = [t_c * (u["lengths"][0] / n_c) ** 2 for u in units]
+    take, acc = 0, 0.0
+    while take < len(units) and acc < target_s:
+        rnd = cost[take:take + nw]
+        acc += max(rnd)
+        take += len(rnd)
+    units = units[:take]
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(nw) as pool:
+        per = pool.map(_oracle_unit, units, chunksize=1)
+    wall = time.perf_counter() - t0
+    flops = sum(bwd_flops(u) for u in units)
+    return {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": int(nw),
+            "workers": int(nw), "cpus_available": int(cpus), "kind": "oracle",
+            "sample": (f"fp64 numpy oracle forward+backward of {len(units)} (sequence, query "
+                       f"head) problems of this workload (sequences cut to their first "
+                       f"{n_cap} rows; D={x['d']}, causal={x['causal']}, window={x['window']}),"
+                       f" a spawn process pool of {nw} workers with 1 BLAS thread each, "
+                       f"{wall:.2f} s wall ({sum(per):.1f} s of worker time); rate = backward "
+                       f"FLOPs of the sample / wall time")}
 
 
 def describe(name: str, x: dict) -> dict:
@@ -426,7 +457,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mha_causal", choices=sorted(ai.WORKLOADS))
+    ap.add_argument("--workload", default="long_gqa", choices=sorted(ai.WORKLOADS))
     ap.add_argument("--n", type=int, default=32768, help="sequence length for mha_causal")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -443,6 +474,17 @@ def main(argv=None) -> int:
               "path shards by (sequence, kv head) with no collective, so N GPUs would each run "
               "this benchmark on their own share.", file=sys.stderr)
         return 2
+    w = ai.workload(args.workload, n=args.n) if args.workload == "mha_causal" else \
+        ai.workload(args.workload)
+    x = ai.generate(w, args.seed)
+    # The CPU baseline runs before anything touches the GPU (its process pool
+    # starts fresh interpreters).  Under a profiler, whose preloaded library
+    # sets up the GPU before this script starts, no worker is started at all.
+    profiled = any(k.startswith("ROCPROF") for k in os.environ) or \
+        "rocprof" in os.environ.get("LD_PRELOAD", "")
+    cpu = None if (args.no_cpu_baseline or args.copy_calibration or profiled) else \
+        cpu_baseline(x)
+
     import torch
 
     if not torch.cuda.is_available():
@@ -458,9 +500,6 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}))
         return 0
 
-    w = ai.workload(args.workload, n=args.n) if args.workload == "mha_causal" else \
-        ai.workload(args.workload)
-    x = ai.generate(w, args.seed)
     # The machine's own ceilings first (they also bring the clocks up after
     # the host-side input generation); then the W warm-up and K timed steps.
     ceiling = atomic_ceiling_gbs()
@@ -524,8 +563,8 @@ def main(argv=None) -> int:
         cases += [(nm, None) for nm in ("varlen_gqa", "sink_window", "long_gqa")
                   if nm != w.name]
         cases = [(nm, n, "thd") for nm, n in cases]
-        if w.name == "mha_causal":  # the same dense batch as [B, H, S, D] tensors
-            cases.append(("mha_causal", args.n, "bhsd"))
+        # the MHA batch of the pages' table again as [B, H, S, D] tensors
+        cases.append(("mha_causal", 32768, "bhsd"))
         for nm, n, layout in cases:
             key = (f"{nm}_n{n}" if n else nm) + ("_bhsd" if layout == "bhsd" else "")
             if args.only_extra is not None and key != args.only_extra:
@@ -550,12 +589,20 @@ def main(argv=None) -> int:
                 "auto_gbs": round(cb / (rr["auto_ms"] * 1e-3) / 1e9, 1),
                 "frac_of_peak": round(cb / (rr["auto_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
             if xx["window"] > 0:
-                extra[key]["attn_bwd_kernel_tflops_nominal_formula"] = round(
-                    bwd_flops_nominal(xx) / (rr["bwd_ms"] * 1e-3) / 1e12, 2)
+                # The stated formula ignores the window: it over-counts the
+                # work 16x here and is no achieved rate (the pair count is).
+                extra[key]["nominal_formula_overcount"] = round(
+                    bwd_flops_nominal(xx) / f, 2)
+            pages = PAGES_BASELINE.get((nm, n)) if layout == "thd" else None
+            if pages:
+                extra[key]["vs_pages_context"] = {
+                    "pages_value": pages, "ratio": round(extra[key]["bwd_tflops"] / pages, 4),
+                    "note": "triton issue 4717, fp16 B4 H8 d64 causal, atomic_add after "
+                            "vectorized atomics, other hardware: context only"}
             print(f"bench: {key}: {extra[key]}", file=sys.stderr, flush=True)
         line["per_workload"] = extra
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(x)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
     return 0
 

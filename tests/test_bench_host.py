@@ -67,35 +67,39 @@ def test_more_than_one_gpu_is_refused(capsys):
     assert "one GPU" in capsys.readouterr().err
 
 
-@pytest.mark.parametrize("nh", [1, 2, 3, 4, 5, 6])
-def test_oracle_sample_keeps_the_head_grouping(nh):
-    # The CPU baseline's sample of query heads [0, nh) must be the same
-    # problem as those heads of the full workload (group size 3 here, so
-    # nh = 4 or 5 only works as whole groups).
+def test_oracle_units_are_the_workload_per_head():
+    # Each CPU-baseline problem (one sequence, one query head, its kv head and
+    # sink) computes exactly that slice of the full workload's oracle run.
     import numpy as np
 
     import attn_inputs as ai
     from oracle import attention as orc
 
-    w = ai.workload("sink_window").with_(seqlens=(24,), hq=6, hkv=2, d=64, window=9)
+    w = ai.workload("sink_window").with_(seqlens=(24, 0, 17), hq=6, hkv=2, d=64, window=9)
     x = ai.generate(w, 0)
-    sub = bench.oracle_sample(x, 24, nh)
-    assert sub["hq"] >= nh and sub["hq"] % sub["hkv"] == 0
-    assert sub["hq"] <= 3 or sub["hq"] % 3 == 0
-    full, part = orc.forward_backward(x), orc.forward_backward(sub)
-    h = sub["hq"]
-    np.testing.assert_allclose(part["dq"], full["dq"][:, :h], rtol=1e-12, atol=1e-12)
-    np.testing.assert_allclose(part["lse"], full["lse"][:h], rtol=1e-12, atol=1e-12)
-    np.testing.assert_allclose(part["dsink"], full["dsink"][:h], rtol=1e-12, atol=1e-12)
+    full = orc.forward_backward(x)
+    units = bench.oracle_units(x, n_cap=1 << 30)
+    assert len(units) == 2 * 6 and [u["lengths"][0] for u in units] == [24] * 6 + [17] * 6
+    cu = x["cu_seqlens"]
+    for i, u in enumerate(units):
+        s, h = (0, i) if i < 6 else (2, i - 6)
+        a, b = cu[s], cu[s + 1]
+        part = orc.forward_backward(u)
+        np.testing.assert_allclose(part["dq"][:, 0], full["dq"][a:b, h], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(part["lse"][0], full["lse"][h, a:b], rtol=1e-12, atol=1e-12)
+    # cut to a prefix: the first n rows as a sequence of their own
+    assert [u["lengths"][0] for u in bench.oracle_units(x, n_cap=8)] == [8] * 12
 
 
 def test_cpu_baseline_covers_the_workload_when_given_time():
     import attn_inputs as ai
 
     w = ai.workload("tiny_gqa")
-    r = bench.cpu_baseline(ai.generate(w, 0), min_run_s=1e9)
-    assert r["kind"] == "oracle" and r["value"] > 0
-    assert f"length {w.seqlens[0]} x {w.hq} query head(s) / {w.hkv} kv head(s)" in r["sample"]
+    r = bench.cpu_baseline(ai.generate(w, 0), target_s=1e9, workers=2)
+    assert r["kind"] == "oracle" and r["value"] > 0 and r["workers"] == 2 and r["cores"] == 2
+    assert r["cpus_available"] >= 1
+    assert "4 (sequence, query head) problems" in r["sample"]
+    assert f"first {w.seqlens[0]} rows" in r["sample"]
 
 
 def test_compulsory_bytes_of_the_window_workload():

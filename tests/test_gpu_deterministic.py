@@ -10,7 +10,7 @@ import attn_inputs as ai
 from oracle import attention as orc
 
 from parity import assert_close, compare_all, outputs, to64
-from test_gpu_parity import EDGE, REDUCED, _announce, _full_compare, _sampled_compare
+from test_gpu_parity import EDGE, REDUCED, _announce, _full_compare
 
 pytestmark = pytest.mark.gpu
 
@@ -72,11 +72,6 @@ def test_against_atomic_path_and_repeatable(w):
 
 def test_full_sink_window():
     _full_compare(ai.workload("sink_window"), row_chunk=256, deterministic=True)
-
-
-@pytest.mark.parametrize("name", ["mha_causal", "long_gqa", "varlen_gqa"])
-def test_full_size_sampled(name):
-    _sampled_compare(ai.workload(name), deterministic=True)
 
 
 @pytest.mark.parametrize("w,conc", [

@@ -2,9 +2,10 @@
 same seeded inputs, element by element.
 
 Small and mid-size cases compare every output element; cases spanning several
-tiles carry ragged tails; the full-size workloads are checked on every
-element where the oracle finishes in seconds (tiny, windowed, varlen) and on
-sampled rows plus exact-sum invariants otherwise.
+tiles carry ragged tails.  The full-size workloads are compared on every
+element too: here the tiny, windowed and short causal ones; the long causal
+sizes, the long-context GQA workload and the varlen batch in
+test_gpu_fullsize.py.
 """
 import numpy as np
 import pytest
@@ -12,7 +13,7 @@ import pytest
 import attn_inputs as ai
 from oracle import attention as orc
 
-from parity import UNIT_ROUNDOFF, assert_close, compare_all, outputs, run_gpu, to64
+from parity import assert_close, compare_all, outputs, run_gpu, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -168,79 +169,6 @@ def test_full_sink_window():
     _full_compare(ai.workload("sink_window"), row_chunk=256)
 
 
-@pytest.mark.slow
-def test_full_varlen_gqa():
-    _full_compare(ai.workload("varlen_gqa"), row_chunk=1024)
-
-
-def _sampled_compare(w, n_q=256, n_k=48, seed=0, k_tail=64, deterministic=False):
-    """Sampled dQ/O/lse/Delta rows anywhere; dK/dV rows among the last
-    `k_tail` keys of each sequence (their query sets are short under the
-    causal mask); exact-sum invariants over all dK / dV rows."""
-    x = ai.generate(w, seed)
-    _announce(f"full-size sampled {w.name} lengths={x['lengths'][:4]}... T={x['cu_seqlens'][-1]} "
-              f"deterministic={deterministic}")
-    inp, ws = run_gpu(x, deterministic=deterministic)
-    got = outputs(ws)
-    rng = np.random.default_rng(1234)
-    T = int(x["cu_seqlens"][-1])
-    qrows = [(int(t), int(h)) for t, h in zip(rng.integers(0, T, n_q), rng.integers(0, w.hq, n_q))]
-    # always include each sequence's first and last token
-    for s in range(len(x["lengths"])):
-        a, b = int(x["cu_seqlens"][s]), int(x["cu_seqlens"][s + 1])
-        if b > a:
-            qrows += [(a, 0), (b - 1, w.hq - 1)]
-    r = orc.query_rows(x, qrows)
-    idx_t = np.array([t for t, _ in qrows])
-    idx_h = np.array([h for _, h in qrows])
-    assert_close(got["o"][idx_t, idx_h], r["o"], "o[sampled]", w.dtype)
-    assert_close(got["lse"][idx_h, idx_t], r["lse"], "lse[sampled]", w.dtype)
-    mass = (np.abs(x["do"][idx_t, idx_h]).astype(np.float64) * np.abs(r["o"])).sum(1)
-    assert_close(got["delta"][idx_h, idx_t], r["delta"], "delta[sampled]", w.dtype,
-                 extra=2.0 * UNIT_ROUNDOFF[w.dtype] * mass)
-    assert_close(got["dq"][idx_t, idx_h], r["dq"], "dq[sampled]", w.dtype)
-    krows = []
-    for s in range(len(x["lengths"])):
-        a, b = int(x["cu_seqlens"][s]), int(x["cu_seqlens"][s + 1])
-        lo = max(a, b - k_tail)
-        picks = rng.integers(lo, b, max(1, n_k // len(x["lengths"])))
-        krows += [(int(t), int(rng.integers(0, w.hkv))) for t in picks]
-        krows += [(b - 1, 0), (lo, w.hkv - 1)]
-    kr = orc.key_rows(x, krows, max_queries=4 * k_tail)
-    kt = np.array([t for t, _ in krows])
-    kg = np.array([g for _, g in krows])
-    assert_close(got["dk"][kt, kg], kr["dk"], "dk[sampled]", w.dtype)
-    assert_close(got["dv"][kt, kg], kr["dv"], "dv[sampled]", w.dtype)
-    # Invariants over every dK / dV row (no sink): per sequence and kv head,
-    # sum_j dV_j = sum_{h in group} sum_i dO_i and sum_j dK_j = 0.  Bound: 1%
-    # of the L1 mass of the summed rows (a dropped or doubled tile moves the
-    # sum by far more).
-    G = w.hq // w.hkv
-    for s in range(len(x["lengths"])):
-        a, b = int(x["cu_seqlens"][s]), int(x["cu_seqlens"][s + 1])
-        for g in range(w.hkv):
-            dvs = got["dv"][a:b, g]
-            want = x["do"][a:b, g * G:(g + 1) * G].astype(np.float64).sum(axis=(0, 1))
-            tol = 1e-2 * np.abs(dvs).sum(0) + 1e-3
-            assert (np.abs(dvs.sum(0) - want) <= tol).all(), ("sum dV", s, g)
-            dks = got["dk"][a:b, g]
-            tol = 1e-2 * np.abs(dks).sum(0) + 1e-3
-            assert (np.abs(dks.sum(0)) <= tol).all(), ("sum dK", s, g)
-
-
 @pytest.mark.parametrize("n", [2048, 4096])
 def test_full_mha_causal_small_n(n):
     _full_compare(ai.workload("mha_causal", n=n), row_chunk=1024)
-
-
-@pytest.mark.parametrize("n", [8192, 16384, 32768])
-def test_full_mha_causal_sampled(n):
-    _sampled_compare(ai.workload("mha_causal", n=n))
-
-
-def test_full_long_gqa_sampled():
-    _sampled_compare(ai.workload("long_gqa"))
-
-
-def test_full_varlen_gqa_sampled():
-    _sampled_compare(ai.workload("varlen_gqa"))
