@@ -27,7 +27,9 @@ __all__ = [
     "attn_bwd_dq_delta",
     "attn_bwd_split",
     "attn_bwd_dkv_reduce",
+    "attn_bwd_static",
     "MAX_SPLIT",
+    "STATIC_SCRATCH_BYTES",
     "attn_abi_version",
     "LIB_PATH",
 ]
@@ -38,6 +40,7 @@ LIB_PATH = os.path.join(_PKG, "libattn_bwd.so")
 ATTN_F16, ATTN_BF16 = 0, 1
 ATTN_LAYOUT_THD, ATTN_LAYOUT_BHSD = 0, 1
 MAX_SPLIT = 16  # ATTN_MAX_SPLIT
+STATIC_SCRATCH_BYTES = 64 * 1024 * 1024  # ATTN_STATIC_SCRATCH_BYTES
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_HIP"}
 
 
@@ -99,6 +102,7 @@ def lib() -> ctypes.CDLL:
             "attn_bwd_dq_delta": [S, P, P, P, P, P, P, P, P, P, P],
             "attn_bwd_split": [S, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P],
             "attn_bwd_dkv_reduce": [S, P, ctypes.c_int32, P, P, P],
+            "attn_bwd_static": [S, P, P, P, P, P, P, P, P, P, P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -360,3 +364,25 @@ def attn_bwd_dkv_reduce(shape: Shape, dkv_partial, nsplit: int, dk, dv, stream=N
     _need(dv, "dv", dt, kvshape(shape))
     _check(lib().attn_bwd_dkv_reduce(ctypes.byref(shape), _ptr(dkv_partial), int(nsplit),
                                      _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def attn_bwd_static(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dq, dk, dv,
+                    stream=None) -> None:
+    """attn_bwd + attn_bwd_postprocess with the fp32 dQ accumulator in the library's own
+    scratch array (no workspace, nothing allocated); writes dq, dk, dv.  Calls that overlap
+    on one GPU race (the array is shared); T * Hq * D * 4 must fit STATIC_SCRATCH_BYTES."""
+    import torch
+
+    T, Hq, Hkv, D, dt = _dims(shape)
+    _need(q, "q", dt, qshape(shape))
+    _need(k, "k", dt, kvshape(shape))
+    _need(v, "v", dt, kvshape(shape))
+    _need(dout, "dout", dt, qshape(shape))
+    _need(lse, "lse", torch.float32, (Hq, T))
+    _need(delta, "delta", torch.float32, (Hq, T))
+    _need(dq, "dq", dt, qshape(shape))
+    _need(dk, "dk", dt, kvshape(shape))
+    _need(dv, "dv", dt, kvshape(shape))
+    _check(lib().attn_bwd_static(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                 _ptr(lse), _ptr(delta), _cu(shape, cu_seqlens), _ptr(dq),
+                                 _ptr(dk), _ptr(dv), _stream(stream)))

@@ -275,6 +275,38 @@ attn_status_t attn_bwd_dkv_reduce(const attn_shape_t* shape, const float* dkv_pa
                     "attn_bwd_dkv_reduce");
 }
 
+attn_status_t attn_bwd_static(const attn_shape_t* shape, const void* q, const void* k,
+                              const void* v, const void* dout, const float* lse,
+                              const float* delta, const int32_t* cu_seqlens, void* dq, void* dk,
+                              void* dv, hipStream_t stream) {
+  attn::Problem p;
+  attn_status_t st = check_shape(shape, cu_seqlens, true, p);
+  if (st != ATTN_OK) return st;
+  REQUIRE_TENSOR(q);
+  REQUIRE_TENSOR(k);
+  REQUIRE_TENSOR(v);
+  REQUIRE_TENSOR(dout);
+  REQUIRE_F32(lse);
+  REQUIRE_F32(delta);
+  REQUIRE_TENSOR(dq);
+  REQUIRE_TENSOR(dk);
+  REQUIRE_TENSOR(dv);
+  const unsigned long long n = (unsigned long long)p.total * p.hq * p.d;
+  REQUIRE(n * 4 <= ATTN_STATIC_SCRATCH_BYTES,
+          "attn_bwd_static: the dQ accumulator needs %llu bytes, more than the %u bytes of the "
+          "library's scratch array (call attn_bwd with a caller-owned dq_accum instead)",
+          n * 4, (unsigned)ATTN_STATIC_SCRATCH_BYTES);
+  if (p.total == 0) return ok();
+  float* acc = nullptr;
+  hipError_t e = attn::static_scratch(&acc);
+  if (e != hipSuccess) return hip_status(e, "attn_bwd_static: scratch array address");
+  e = attn::launch_zero(acc, (size_t)n, stream);
+  if (e != hipSuccess) return hip_status(e, "attn_bwd_static: clearing the accumulator");
+  e = attn::launch_bwd(p, q, k, v, dout, lse, delta, cu_seqlens, acc, dk, dv, stream);
+  if (e != hipSuccess) return hip_status(e, "attn_bwd_static: main pass");
+  return hip_status(attn::launch_postprocess(p, acc, dq, stream), "attn_bwd_static: cast");
+}
+
 attn_status_t attn_bwd_postprocess(const attn_shape_t* shape, const float* dq_accum, void* dq,
                                    hipStream_t stream) {
   attn::Problem p;

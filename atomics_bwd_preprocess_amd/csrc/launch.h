@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/attn_bwd.h"
+
 namespace attn {
 
 struct Problem {
@@ -73,5 +75,15 @@ hipError_t launch_dkv_reduce(const Problem& p, const float* dkv_part, int nsplit
 
 hipError_t launch_postprocess(const Problem& p, const float* dq_accum, void* dq,
                               hipStream_t stream);
+
+// Size of the library-owned scratch array (scratch.hip), in bytes.
+constexpr size_t kStaticScratchBytes = ATTN_STATIC_SCRATCH_BYTES;
+
+// Device address of this device's scratch array (taken on the first call on
+// the device, then cached per device).
+hipError_t static_scratch(float** ptr);
+
+// Zero n floats at p (n a multiple of 4, p 16-byte aligned) with a fill kernel.
+hipError_t launch_zero(float* p, size_t n, hipStream_t stream);
 
 }  // namespace attn

@@ -65,8 +65,11 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 #define ATTN_MAX_SPLIT 16 /* largest nsplit of attn_bwd_split */
+/* Bytes of the library-owned scratch array attn_bwd_static accumulates dQ in
+   (64 MiB per GPU the library runs on). */
+#define ATTN_STATIC_SCRATCH_BYTES (64u * 1024u * 1024u)
 
 typedef enum {
   ATTN_OK = 0,
@@ -224,6 +227,32 @@ attn_status_t attn_bwd_split(const attn_shape_t* shape, const void* q, const voi
  */
 attn_status_t attn_bwd_dkv_reduce(const attn_shape_t* shape, const float* dkv_partial,
                                   int32_t nsplit, void* dk, void* dv, hipStream_t stream);
+
+/*
+ * attn_bwd followed by attn_bwd_postprocess, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the fp32 dQ accumulator is not a caller workspace but a
+ * library-owned device array of ATTN_STATIC_SCRATCH_BYTES per GPU, held from
+ * library load until the process ends.  The call zeroes that accumulator
+ * with a fill kernel, runs the main pass into it and casts it into dq
+ * (storage dtype, RNE of scale * accumulator), all on `stream`; it allocates
+ * nothing and calls no allocating routine.  Inputs and outputs are the
+ * caller's as for attn_bwd (delta from attn_bwd_preprocess, which may be
+ * called with dq_accum = NULL); dq, dk, dv are written.
+ *  - Size limit: total_tokens * hq * head_dim * 4 bytes must not exceed
+ *    ATTN_STATIC_SCRATCH_BYTES, else ATTN_ERR_INVALID_ARG before any launch.
+ *  - Every call on one GPU uses that GPU's single array: calls that overlap
+ *    on one GPU (different streams, or host threads) race and give wrong dQ.
+ *    Serialise them (one stream, or events).
+ *  - The first call on a device looks up the array's device address (no
+ *    allocation); a failure there is ATTN_ERR_HIP.
+ * Results equal attn_bwd + attn_bwd_postprocess (dQ within the atomic
+ * summation-order variation; dk, dv bitwise).
+ */
+attn_status_t attn_bwd_static(const attn_shape_t* shape, const void* q, const void* k,
+                              const void* v, const void* dout, const float* lse,
+                              const float* delta, const int32_t* cu_seqlens, void* dq, void* dk,
+                              void* dv, hipStream_t stream);
 
 /*
  * Backward postprocess ([ASC] postprocess kernel casting the fp32 gradient

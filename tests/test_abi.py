@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
     assert _declared() == sorted(["attn_fwd", "attn_bwd_preprocess", "attn_bwd",
                                   "attn_bwd_postprocess", "attn_bwd_dkdv", "attn_bwd_dq",
                                   "attn_bwd_split", "attn_bwd_dkv_reduce", "attn_bwd_dsink",
-                                  "attn_bwd_dq_delta",
+                                  "attn_bwd_dq_delta", "attn_bwd_static",
                                   "attn_status_string", "attn_last_error",
                                   "attn_abi_version"])
 
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     L = ab.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert ab.attn_abi_version() == 5
+    assert ab.attn_abi_version() == 6
     assert ab.MAX_SPLIT == int(re.search(r"#define ATTN_MAX_SPLIT (\d+)", open(HEADER).read()).group(1))
     assert L.attn_status_string(0) == b"ok"
     assert L.attn_status_string(1) == b"invalid argument"
@@ -198,3 +198,23 @@ def test_dq_delta_rejects_bad_pointers_before_any_launch():
     bad[3] = FAKE + 8  # o misaligned
     assert L.attn_bwd_dq_delta(ctypes.byref(s), *bad, None) == 1
     assert L.attn_bwd_dq_delta(ctypes.byref(_shape(head_dim=96)), *args, None) == 2
+
+
+def test_static_scratch_entry_rejects_before_any_launch():
+    L = ab.lib()
+    m = re.search(r"#define ATTN_STATIC_SCRATCH_BYTES \((\d+)u \* (\d+)u \* (\d+)u\)",
+                  open(HEADER).read())
+    assert ab.STATIC_SCRATCH_BYTES == int(m.group(1)) * int(m.group(2)) * int(m.group(3))
+    # 4096 tokens x 64 heads x 128 dims x 4 bytes = 128 MiB > the 64 MiB array
+    big = _shape(num_seqs=1, max_seqlen=4096, total_tokens=4096, hq=64, hkv=8, head_dim=128)
+    args = [FAKE] * 6 + [None] + [FAKE] * 3
+    assert L.attn_bwd_static(ctypes.byref(big), *args, None) == 1
+    assert b"scratch array" in L.attn_last_error()
+    # a missing output is rejected; an empty problem launches nothing
+    s = _shape()
+    bad = list(args)
+    bad[7] = None  # dq
+    assert L.attn_bwd_static(ctypes.byref(s), *bad, None) == 1
+    assert b"dq is NULL" in L.attn_last_error()
+    e = _shape(total_tokens=0)
+    assert L.attn_bwd_static(ctypes.byref(e), *args[:6], FAKE, *args[7:], None) == 0
