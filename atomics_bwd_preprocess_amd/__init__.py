@@ -28,6 +28,8 @@ __all__ = [
     "attn_bwd_split",
     "attn_bwd_dkv_reduce",
     "attn_bwd_static",
+    "attn_bwd_fused_cast",
+    "fused_cast_counters",
     "MAX_SPLIT",
     "STATIC_SCRATCH_BYTES",
     "attn_abi_version",
@@ -103,6 +105,7 @@ def lib() -> ctypes.CDLL:
             "attn_bwd_split": [S, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P],
             "attn_bwd_dkv_reduce": [S, P, ctypes.c_int32, P, P, P],
             "attn_bwd_static": [S, P, P, P, P, P, P, P, P, P, P, P],
+            "attn_bwd_fused_cast": [S, P, P, P, P, P, P, P, P, P, P, P, P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -386,3 +389,34 @@ def attn_bwd_static(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dq, dk,
     _check(lib().attn_bwd_static(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                                  _ptr(lse), _ptr(delta), _cu(shape, cu_seqlens), _ptr(dq),
                                  _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def fused_cast_counters(shape: Shape) -> int:
+    """ATTN_FUSED_CAST_COUNTERS: int32 arrival counters attn_bwd_fused_cast needs."""
+    n = shape.num_seqs * shape.hq * ((shape.max_seqlen + 31) // 32)
+    return (n + 3) // 4 * 4
+
+
+def attn_bwd_fused_cast(shape: Shape, q, k, v, dout, lse, delta, cu_seqlens, dq_accum, counters,
+                        dq, dk, dv, stream=None) -> None:
+    """attn_bwd + attn_bwd_postprocess in one pass for causal problems: the last workgroup
+    contributing to a query block casts it (arrival counters, zeroed by the call); writes
+    dq, dk, dv.  dq_accum must have been zeroed by attn_bwd_preprocess."""
+    import torch
+
+    T, Hq, Hkv, D, dt = _dims(shape)
+    _need(q, "q", dt, qshape(shape))
+    _need(k, "k", dt, kvshape(shape))
+    _need(v, "v", dt, kvshape(shape))
+    _need(dout, "dout", dt, qshape(shape))
+    _need(lse, "lse", torch.float32, (Hq, T))
+    _need(delta, "delta", torch.float32, (Hq, T))
+    _need(dq_accum, "dq_accum", torch.float32, qshape(shape))
+    _need(counters, "counters", torch.int32, (fused_cast_counters(shape),))
+    _need(dq, "dq", dt, qshape(shape))
+    _need(dk, "dk", dt, kvshape(shape))
+    _need(dv, "dv", dt, kvshape(shape))
+    _check(lib().attn_bwd_fused_cast(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                     _ptr(lse), _ptr(delta), _cu(shape, cu_seqlens),
+                                     _ptr(dq_accum), _ptr(counters), _ptr(dq), _ptr(dk),
+                                     _ptr(dv), _stream(stream)))

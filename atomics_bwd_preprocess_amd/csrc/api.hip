@@ -177,6 +177,40 @@ attn_status_t attn_bwd(const attn_shape_t* shape, const void* q, const void* k, 
                     "attn_bwd");
 }
 
+attn_status_t attn_bwd_fused_cast(const attn_shape_t* shape, const void* q, const void* k,
+                                  const void* v, const void* dout, const float* lse,
+                                  const float* delta, const int32_t* cu_seqlens, float* dq_accum,
+                                  int32_t* counters, void* dq, void* dk, void* dv,
+                                  hipStream_t stream) {
+  attn::Problem p;
+  attn_status_t st = check_shape(shape, cu_seqlens, true, p);
+  if (st != ATTN_OK) return st;
+  REQUIRE_TENSOR(q);
+  REQUIRE_TENSOR(k);
+  REQUIRE_TENSOR(v);
+  REQUIRE_TENSOR(dout);
+  REQUIRE_F32(lse);
+  REQUIRE_F32(delta);
+  REQUIRE_TENSOR(dq_accum);
+  REQUIRE_TENSOR(counters);
+  REQUIRE_TENSOR(dq);
+  REQUIRE_TENSOR(dk);
+  REQUIRE_TENSOR(dv);
+  if (p.total == 0) return ok();
+  hipError_t e;
+  if (!p.causal || p.bhsd) {
+    e = attn::launch_bwd(p, q, k, v, dout, lse, delta, cu_seqlens, dq_accum, dk, dv, stream);
+    if (e != hipSuccess) return hip_status(e, "attn_bwd_fused_cast: main pass");
+    return hip_status(attn::launch_postprocess(p, dq_accum, dq, stream), "attn_bwd_fused_cast: cast");
+  }
+  const long long n = ATTN_FUSED_CAST_COUNTERS(p.num_seqs, p.hq, p.max_seqlen);
+  e = attn::launch_zero(reinterpret_cast<float*>(counters), (size_t)n, stream);
+  if (e != hipSuccess) return hip_status(e, "attn_bwd_fused_cast: clearing the counters");
+  return hip_status(attn::launch_bwd_fused_cast(p, q, k, v, dout, lse, delta, cu_seqlens, dq_accum,
+                                                counters, dq, dk, dv, stream),
+                    "attn_bwd_fused_cast");
+}
+
 attn_status_t attn_bwd_dkdv(const attn_shape_t* shape, const void* q, const void* k,
                             const void* v, const void* dout, const float* lse,
                             const float* delta, const int32_t* cu_seqlens, void* dk, void* dv,

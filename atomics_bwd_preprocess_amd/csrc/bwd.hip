@@ -138,7 +138,30 @@ struct BwdArgs {
   float* dkv_part;  // SPLIT: fp32 partials [nsplit][2][dk-shaped]
   int nsplit;
   int lpt;  // rank the (sequence, key block) items longest first (ragged batches)
+  // Fused dQ cast (causal problems, unsplit atomic pass): arrival counters
+  // per (sequence, query head, query block), zeroed before the launch, and
+  // the 16-bit dQ the last contributing workgroup of a block casts into.
+  int* counters;
+  void* dq;
 };
+
+// Number of key-block workgroups whose pair loop contains query block qb of
+// a causal sequence of length L: key blocks jb with jb * BN / BM <= qb (the
+// loop starts at the block's first key) and qb below the loop's end, which a
+// window places at (last key of jb + W - 1) / BM + 1.  The same bounds the
+// loop uses, evaluated from the query side.
+__device__ __forceinline__ int cast_contributors(int qb, int L, int BM, int BN, int window) {
+  const int jb_hi = (qb * BM) / BN;
+  if (window <= 0) return jb_hi + 1;
+  const int nqb = (L + BM - 1) / BM;
+  int cnt = 0;
+  for (int jb = jb_hi; jb >= 0; --jb) {
+    const int kv_last = min(L, jb * BN + BN) - 1;
+    if (qb >= min(nqb, (kv_last + window - 1) / BM + 1)) break;  // the end only moves down
+    ++cnt;
+  }
+  return cnt;
+}
 
 // Longest-first order for ragged batches.  Key-block index slowest is
 // longest first only when every sequence has the same length; otherwise a
@@ -206,7 +229,8 @@ __device__ __forceinline__ int dst_off(int r, int q) {  // q: multiple of 4
 // with the query-stationary dQ pass): no dS tile in LDS, no atomics.
 // BHSD: [B, H, S, D] tensors instead of packed [T, H, D].
 // SPLIT: pairs of a key block split over p.nsplit workgroups (see above).
-template <typename T, int D, bool WIN, bool DQ, bool BHSD, bool SPLIT>
+// CAST: the fused dQ cast epilogue (p.counters, p.dq; causal, unsplit, packed).
+template <typename T, int D, bool WIN, bool DQ, bool BHSD, bool SPLIT, bool CAST = false>
 __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void bwd_kernel(BwdArgs p) {
   constexpr int NW = nw_of(DQ, SPLIT);
   using C = Cfg<D, NW, DQ>;
@@ -699,11 +723,69 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
         buf_store_b16(dkr, off, bits16(to16<T>(dk[kt][t][r] * p.scale)));
         buf_store_b16(dvr, off, bits16(to16<T>(dv[kt][t][r])));
       }
+
+  // ---- fused dQ cast (causal problems): count this workgroup's arrival at
+  // every (query head, query block) it sent atomics to, once all of them are
+  // performed; the last contributor of a block casts it.  Workgroup-uniform.
+  if constexpr (CAST) {
+    {
+      __threadfence();  // this thread's atomics are performed device-wide
+      __syncthreads();  // ... for every thread of the workgroup
+      int* list = reinterpret_cast<int*>(smem);  // the pair loop is done with LDS
+      int* count = list + kThreads;
+      const int nqb_max = (p.max_seqlen + BM - 1) / BM;
+      for (int base = 0; base < npairs; base += kThreads) {
+        if (tid == 0) *count = 0;
+        __syncthreads();
+        const int i = base + tid;
+        if (i < npairs) {
+          const int hh = g * G + i / nq, qb = ib0 + i % nq;
+          int* ctr = p.counters + ((size_t)s * p.hq + hh) * nqb_max + qb;
+          if (atomicAdd(ctr, 1) + 1 == cast_contributors(qb, L, BM, kBN, p.window))
+            list[atomicAdd(count, 1)] = i;
+        }
+        __syncthreads();
+        const int ncast = *count;
+        if (ncast > 0) {
+          __threadfence();  // acquire: every contributor's atomics are visible
+          for (int t = 0; t < ncast; ++t) {
+            const int it = list[t];
+            const int hh = g * G + it / nq, q0 = (ib0 + it % nq) * BM;
+            const int rows = min(L - q0, BM);
+            for (int e = tid; e < rows * (D / 4); e += kThreads) {
+              const int r = e / (D / 4), c4 = e % (D / 4);
+              const size_t off = row_off<D, BHSD>(a, q0 + r, hh, p.hq, p.max_seqlen) + 4 * c4;
+              const float4 v4 = *reinterpret_cast<const float4*>(p.dq_accum + off);
+              T4 o4;
+              o4[0] = to16<T>(v4.x * p.scale);
+              o4[1] = to16<T>(v4.y * p.scale);
+              o4[2] = to16<T>(v4.z * p.scale);
+              o4[3] = to16<T>(v4.w * p.scale);
+              st8<T>(static_cast<T*>(p.dq) + off, o4);
+            }
+          }
+        }
+        __syncthreads();  // the list is rewritten next round
+      }
+    }
+  }
 }
 
 template <typename T, int D, bool DQ, bool BHSD>
 hipError_t bwd_t2(const BwdArgs& args, unsigned blocks, int threads, hipStream_t stream) {
   const dim3 grid(blocks), block(threads);
+  if constexpr (DQ && !BHSD) {
+    if (args.counters) {
+      if (args.window > 0)
+        hipLaunchKernelGGL((bwd_kernel<T, D, true, true, false, false, true>), grid, block, 0,
+                           stream, args);
+      else
+        hipLaunchKernelGGL((bwd_kernel<T, D, false, true, false, false, true>), grid, block, 0,
+                           stream, args);
+      return hipGetLastError();
+    }
+  }
+  if (args.counters) return hipErrorInvalidValue;  // no fused cast for this variant
   // The split kernel is built without the window specialisation (it is
   // still correct for windows, whose key blocks are short anyway).
   if (args.dkv_part)
@@ -726,7 +808,8 @@ template <bool DQ>
 hipError_t bwd_dispatch(const Problem& p, const void* q, const void* k, const void* v,
                         const void* dout, const float* lse, const float* delta,
                         const int32_t* cu, float* dq_accum, void* dk, void* dv,
-                        float* dkv_part, int nsplit, hipStream_t stream) {
+                        float* dkv_part, int nsplit, hipStream_t stream,
+                        int* counters = nullptr, void* dq = nullptr) {
   BwdArgs a;
   a.q = q;
   a.k = k;
@@ -749,6 +832,8 @@ hipError_t bwd_dispatch(const Problem& p, const void* q, const void* k, const vo
   a.scale_log2 = p.scale * kLog2e;
   a.dkv_part = dkv_part;
   a.nsplit = nsplit;
+  a.counters = counters;
+  a.dq = dq;
   // The variant bwd_t2 picks fixes the workgroup: nw_of waves, 32 keys each.
   const int nw = nw_of(DQ, dkv_part != nullptr);
   const int bn = nw * 32 * kKT;
@@ -771,6 +856,14 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
                       const int32_t* cu, float* dq_accum, void* dk, void* dv,
                       hipStream_t stream) {
   return bwd_dispatch<true>(p, q, k, v, dout, lse, delta, cu, dq_accum, dk, dv, nullptr, 1, stream);
+}
+
+hipError_t launch_bwd_fused_cast(const Problem& p, const void* q, const void* k, const void* v,
+                                const void* dout, const float* lse, const float* delta,
+                                const int32_t* cu, float* dq_accum, int* counters, void* dq,
+                                void* dk, void* dv, hipStream_t stream) {
+  return bwd_dispatch<true>(p, q, k, v, dout, lse, delta, cu, dq_accum, dk, dv, nullptr, 1, stream,
+                            counters, dq);
 }
 
 hipError_t launch_bwd_dkdv(const Problem& p, const void* q, const void* k, const void* v,

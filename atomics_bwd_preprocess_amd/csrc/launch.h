@@ -49,6 +49,14 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
                       const int32_t* cu, float* dq_accum, void* dk, void* dv,
                       hipStream_t stream);
 
+// Main pass (causal problems) that also casts dQ: per (sequence, query
+// head, query block) arrival counters (zeroed before the launch) let the last
+// contributing workgroup of a block write scale * dq_accum into dq.
+hipError_t launch_bwd_fused_cast(const Problem& p, const void* q, const void* k, const void* v,
+                                const void* dout, const float* lse, const float* delta,
+                                const int32_t* cu, float* dq_accum, int* counters, void* dq,
+                                void* dk, void* dv, hipStream_t stream);
+
 // Main pass without its dQ product (dK / dV only).
 hipError_t launch_bwd_dkdv(const Problem& p, const void* q, const void* k, const void* v,
                            const void* dout, const float* lse, const float* delta,

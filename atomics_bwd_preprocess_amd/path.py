@@ -26,9 +26,9 @@ from typing import Optional
 import torch
 
 from . import (MAX_SPLIT, Shape, attn_bwd, attn_bwd_dkdv, attn_bwd_dkv_reduce, attn_bwd_dq,
-               attn_bwd_dq_delta, attn_bwd_dsink,
+               attn_bwd_dq_delta, attn_bwd_dsink, attn_bwd_fused_cast,
                attn_bwd_postprocess, attn_bwd_preprocess, attn_bwd_split, attn_fwd,
-               dkv_partial_shape, kvshape, qshape)
+               dkv_partial_shape, fused_cast_counters, kvshape, qshape)
 
 DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -63,6 +63,7 @@ class Workspace:
     dv: torch.Tensor
     dsink: Optional[torch.Tensor]
     dkv_part: Optional[torch.Tensor] = None  # fp32 partials of a split backward
+    counters: Optional[torch.Tensor] = None  # arrival counters of the fused dQ cast
 
 
 def to_device(x: dict, device="cuda", layout="thd") -> Inputs:
@@ -248,8 +249,15 @@ def forward(inp: Inputs, ws: Workspace, stream=None) -> None:
     attn_fwd(inp.shape, inp.q, inp.k, inp.v, inp.cu, inp.sink, ws.o, ws.lse, stream)
 
 
+def _counters(inp: Inputs, ws: Workspace) -> torch.Tensor:
+    n = fused_cast_counters(inp.shape)
+    if ws.counters is None or ws.counters.numel() != n:
+        ws.counters = torch.empty(n, device=inp.q.device, dtype=torch.int32)
+    return ws.counters
+
+
 def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
-             mode: str = "atomic", kv_splits=1) -> str:
+             mode: str = "atomic", kv_splits=1, fused_cast: bool = False) -> str:
     """Preprocess -> main backward -> postprocess; O and lse default to ws.o / ws.lse.
 
     mode "deterministic": query-stationary dQ pass + dK/dV pass, no atomics
@@ -260,7 +268,9 @@ def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
     splits every key block's pairs over that many workgroups, whose fp32
     dK / dV partials are then summed in a fixed order (attn_bwd_split +
     attn_bwd_dkv_reduce; the partials live in ws.dkv_part, allocated on first
-    use).  Returns the mode that ran."""
+    use).  fused_cast (atomic mode, unsplit): the main pass casts dQ itself
+    (attn_bwd_fused_cast; arrival counters in ws.counters, allocated on first
+    use) instead of a separate postprocess.  Returns the mode that ran."""
     if mode == "auto":
         mode = select_mode(inp.shape, inp.lengths)
     if mode not in ("atomic", "deterministic"):
@@ -301,6 +311,9 @@ def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
     elif det:
         attn_bwd_dkdv(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dk,
                       ws.dv, stream)
+    elif fused_cast:
+        attn_bwd_fused_cast(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu,
+                            ws.dq_accum, _counters(inp, ws), ws.dq, ws.dk, ws.dv, stream)
     else:
         attn_bwd(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu,
                  ws.dq_accum, ws.dk, ws.dv, stream)
@@ -308,7 +321,7 @@ def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
         attn_bwd_dsink(inp.shape, lse, ws.delta, inp.sink, ws.dsink, stream)
     if conc:
         main.wait_stream(side)
-    elif not det:
+    elif not det and not (fused_cast and kv_splits == 1):
         attn_bwd_postprocess(inp.shape, ws.dq_accum, ws.dq, stream)
     return mode
 

@@ -250,7 +250,8 @@ def run_gpu(x: dict, steps: int, warmup: int, layout: str = "thd", warm_s: float
     import torch
 
     from atomics_bwd_preprocess_amd import (attn_bwd, attn_bwd_dkdv, attn_bwd_dq,
-                                            attn_bwd_postprocess, attn_bwd_preprocess, path)
+                                            attn_bwd_fused_cast, attn_bwd_postprocess,
+                                            attn_bwd_preprocess, fused_cast_counters, path)
 
     inp = path.to_device(x, "cuda", layout=layout)
     ws = path.workspace(inp)
@@ -281,6 +282,30 @@ def run_gpu(x: dict, steps: int, warmup: int, layout: str = "thd", warm_s: float
                bwd_ms=float(mean[2]), post_ms=float(mean[3]),
                bwd_ms_min=float(ms[:, 2].min()), bwd_ms_median=float(np.median(ms[:, 2])))
     out["steps"] = steps
+    # The same backward with the dQ cast fused into the main pass (the last
+    # workgroup contributing to a query block casts it; causal problems).
+    counters = torch.empty(fused_cast_counters(inp.shape), dtype=torch.int32, device="cuda")
+
+    def fused():
+        attn_bwd_preprocess(inp.shape, ws.o, inp.do, ws.lse, inp.cu, inp.sink, ws.delta,
+                            ws.dq_accum, ws.dsink)
+        attn_bwd_fused_cast(inp.shape, inp.q, inp.k, inp.v, inp.do, ws.lse, ws.delta, inp.cu,
+                            ws.dq_accum, counters, ws.dq, ws.dk, ws.dv)
+
+    _warm(fused, 2, warm_s)
+    for i in range(steps):
+        e = ev[i]
+        e[0].record(stream)
+        attn_bwd_preprocess(inp.shape, ws.o, inp.do, ws.lse, inp.cu, inp.sink, ws.delta,
+                            ws.dq_accum, ws.dsink)
+        e[1].record(stream)
+        attn_bwd_fused_cast(inp.shape, inp.q, inp.k, inp.v, inp.do, ws.lse, ws.delta, inp.cu,
+                            ws.dq_accum, counters, ws.dq, ws.dk, ws.dv)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    fm = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(2)] for e in ev]).mean(axis=0)
+    out.update(fc_pre_ms=float(fm[0]), fc_bwd_ms=float(fm[1]))
+    del counters
     # The deterministic backward on the same inputs: preprocess without the
     # accumulator, the dK/dV-only main pass, the query-stationary dQ pass.
     _warm(lambda: path.backward(inp, ws, mode="deterministic"), 2, warm_s)
@@ -344,6 +369,20 @@ def deterministic_entry(x: dict, r: dict) -> dict:
             "attn_bwd_dq_tflops": round(0.6 * f / (r["dq_ms"] * 1e-3) / 1e12, 2),
             "vs_atomic_path": round((r["pre_ms"] + r["bwd_ms"] + r["post_ms"]) / conc, 4),
             "auto_mode": r["auto_mode"]}
+
+
+def fused_cast_entry(x: dict, r: dict) -> dict:
+    """The atomic backward with the dQ cast fused into the main pass
+    (attn_bwd_fused_cast; for non-causal problems it runs the separate cast
+    itself): its kernel time, the backward (preprocess + that pass), and the
+    ratio of the separate-cast backward (preprocess + attn_bwd + postprocess)
+    to it."""
+    sep = r["pre_ms"] + r["bwd_ms"] + r["post_ms"]
+    tot = r["fc_pre_ms"] + r["fc_bwd_ms"]
+    return {"attn_bwd_fused_cast_ms": round(r["fc_bwd_ms"], 4), "bwd_ms": round(tot, 4),
+            "bwd_tflops": round(bwd_flops(x) / (tot * 1e-3) / 1e12, 2),
+            "separate_cast_bwd_ms": round(sep, 4),
+            "vs_separate_cast": round(sep / tot, 4)}
 
 
 def auto_entry(x: dict, r: dict) -> dict:
@@ -549,6 +588,7 @@ def main(argv=None) -> int:
                             "their device-wide rate, not the MFMA peak, bounds this kernel"},
         "wall_ms_per_step": round(r["wall_ms_per_step"], 4),
         "deterministic": deterministic_entry(x, r),
+        "fused_cast": fused_cast_entry(x, r),
         "auto": auto_entry(x, r),
         "device": device_info(),
     }
@@ -582,6 +622,7 @@ def main(argv=None) -> int:
                           "fwd_tflops": round(fwd_flops(xx) / (rr["fwd_ms"] * 1e-3) / 1e12, 2),
                           "attn_fwd_ms": round(rr["fwd_ms"], 4), "timed_steps": rr["steps"]}
             extra[key]["deterministic"] = deterministic_entry(xx, rr)
+            extra[key]["fused_cast"] = fused_cast_entry(xx, rr)
             extra[key]["auto"] = auto_entry(xx, rr)
             cb = compulsory_bytes(xx)
             extra[key]["hbm_floor"] = {

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 #define ATTN_MAX_SPLIT 16 /* largest nsplit of attn_bwd_split */
 /* Bytes of the library-owned scratch array attn_bwd_static accumulates dQ in
    (64 MiB per GPU the library runs on). */
@@ -162,6 +162,38 @@ attn_status_t attn_bwd(const attn_shape_t* shape, const void* q, const void* k, 
                        const void* dout, const float* lse, const float* delta,
                        const int32_t* cu_seqlens, float* dq_accum, void* dk, void* dv,
                        hipStream_t stream);
+
+/*
+ * Number of int32 arrival counters attn_bwd_fused_cast needs: one per
+ * (sequence, query head, block of 32 query rows), rounded up to a multiple
+ * of 4.
+ */
+#define ATTN_FUSED_CAST_COUNTERS(num_seqs, hq, max_seqlen) \
+  (((long long)(num_seqs) * (hq) * (((max_seqlen) + 31) / 32) + 3) / 4 * 4)
+
+/*
+ * attn_bwd and attn_bwd_postprocess in one pass, for causal problems
+ * ([ASC] names the separate postprocess, and the host-side cast of its fp32
+ * dK/dV atomics, as costs it could not remove; on this part the cast needs
+ * no host sync and can live in the main pass).  dq_accum is zeroed by
+ * attn_bwd_preprocess as for attn_bwd.  The call zeroes `counters`
+ * (int32[ATTN_FUSED_CAST_COUNTERS(...)], caller-owned, 16-byte aligned) and
+ * runs the main pass; every key-block workgroup, after its last dQ atomics
+ * are performed device-wide, counts one arrival at each (query head, query
+ * block) it contributed to, and the workgroup whose arrival completes a
+ * block's count (the number of key blocks whose loop contains it, known in
+ * closed form) reads that block's rows of dq_accum and writes
+ * dq = RNE(scale * dq_accum).  dk and dv are written as by attn_bwd.
+ * Non-causal problems (where the last finisher of a sequence would cast all
+ * of it alone) and the [B, H, S, D] layout run attn_bwd followed by the
+ * separate cast instead; the results are the same either way.  dq_accum
+ * holds dQ / scale afterwards.
+ */
+attn_status_t attn_bwd_fused_cast(const attn_shape_t* shape, const void* q, const void* k,
+                                  const void* v, const void* dout, const float* lse,
+                                  const float* delta, const int32_t* cu_seqlens, float* dq_accum,
+                                  int32_t* counters, void* dq, void* dk, void* dv,
+                                  hipStream_t stream);
 
 /*
  * Deterministic backward, pass 1 of 2: the main pass above without its dQ

@@ -64,9 +64,10 @@ def delta_extra(x: dict, o_ref: np.ndarray, dtype: str) -> np.ndarray:
     return 2.0 * UNIT_ROUNDOFF[dtype] * mass
 
 
-def run_gpu(x: dict, device="cuda", o=None, lse=None, deterministic=False):
+def run_gpu(x: dict, device="cuda", o=None, lse=None, deterministic=False, fused_cast=False):
     """Run forward + backward on the HIP path; returns (inputs, workspace).
-    deterministic: the atomic-free backward (dK/dV pass + query-stationary dQ)."""
+    deterministic: the atomic-free backward (dK/dV pass + query-stationary dQ);
+    fused_cast: the atomic backward casting dQ in its main pass."""
     import torch
 
     from atomics_bwd_preprocess_amd import path
@@ -78,9 +79,9 @@ def run_gpu(x: dict, device="cuda", o=None, lse=None, deterministic=False):
     if o is not None:
         o_t = torch.from_numpy(np.ascontiguousarray(o, dtype=np.float32)).to(device).to(inp.q.dtype)
         lse_t = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).to(device)
-        path.backward(inp, ws, o=o_t, lse=lse_t, mode=mode)
+        path.backward(inp, ws, o=o_t, lse=lse_t, mode=mode, fused_cast=fused_cast)
     else:
-        path.backward(inp, ws, mode=mode)
+        path.backward(inp, ws, mode=mode, fused_cast=fused_cast)
     torch.cuda.synchronize()
     return inp, ws
 

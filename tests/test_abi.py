@@ -29,6 +29,7 @@ def test_header_declares_the_boundary():
                                   "attn_bwd_postprocess", "attn_bwd_dkdv", "attn_bwd_dq",
                                   "attn_bwd_split", "attn_bwd_dkv_reduce", "attn_bwd_dsink",
                                   "attn_bwd_dq_delta", "attn_bwd_static",
+                                  "attn_bwd_fused_cast",
                                   "attn_status_string", "attn_last_error",
                                   "attn_abi_version"])
 
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
     L = ab.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert ab.attn_abi_version() == 6
+    assert ab.attn_abi_version() == 7
     assert ab.MAX_SPLIT == int(re.search(r"#define ATTN_MAX_SPLIT (\d+)", open(HEADER).read()).group(1))
     assert L.attn_status_string(0) == b"ok"
     assert L.attn_status_string(1) == b"invalid argument"
@@ -218,3 +219,21 @@ def test_static_scratch_entry_rejects_before_any_launch():
     assert b"dq is NULL" in L.attn_last_error()
     e = _shape(total_tokens=0)
     assert L.attn_bwd_static(ctypes.byref(e), *args[:6], FAKE, *args[7:], None) == 0
+
+
+def test_fused_cast_validation():
+    L, s = ab.lib(), _shape()
+    args = [FAKE] * 6 + [None] + [FAKE] * 5
+    bad = list(args)
+    bad[8] = None  # counters
+    assert L.attn_bwd_fused_cast(ctypes.byref(s), *bad, None) == 1
+    assert b"counters is NULL" in L.attn_last_error()
+    bad = list(args)
+    bad[7] = FAKE + 4  # dq_accum misaligned
+    assert L.attn_bwd_fused_cast(ctypes.byref(s), *bad, None) == 1
+    e = _shape(total_tokens=0)
+    assert L.attn_bwd_fused_cast(ctypes.byref(e), *args[:6], FAKE, *args[7:], None) == 0
+    # the counter count follows the header's macro (blocks of 32 query rows, multiple of 4)
+    sh = ab.Shape.make(num_seqs=3, max_seqlen=100, total_tokens=300, hq=5, hkv=1, head_dim=64,
+                       causal=True, window=0, scale=0.125, dtype="f16")
+    assert ab.fused_cast_counters(sh) == 60

@@ -5,11 +5,12 @@ and the MHA causal sweep (4 x N, 8 heads, D = 64, fp16) at N = 8192, 16384
 and 32768 on one whole sequence with all 8 heads, plus the ragged varlen
 batch on every element.
 
-Each case runs the HIP path once per dQ orientation (region-wide fp32
-atomics, and the query-stationary deterministic passes) at the full size, in
-the configuration the benchmark times, then computes the fp64 oracle for the
+Each case runs the HIP path once per dQ variant (region-wide fp32 atomics
+with the separate cast, the same with the cast fused into the main pass, and
+the query-stationary deterministic passes) at the full size, in the
+configuration the benchmark times, then computes the fp64 oracle for the
 selection once, one (sequence, head) problem per worker thread, and compares
-O, lse, Delta, dQ, dK and dV element by element for both orientations."""
+O, lse, Delta, dQ, dK and dV element by element for every variant."""
 import time
 
 import numpy as np
@@ -44,9 +45,10 @@ def _check_every_element(w, seqs, groups, row_chunk=1024):
     _log(f"{w.name} lengths={x['lengths'][:8]} hq={w.hq} hkv={w.hkv} d={w.d} {w.dtype} "
          f"sequences={list(seqs)} kv groups={list(groups)}")
     got = {}
-    for mode in ("atomic", "deterministic"):
+    for mode in ("atomic", "deterministic", "fused_cast"):
         _log(f"GPU {mode}")
-        inp, ws = run_gpu(x, deterministic=(mode == "deterministic"))
+        inp, ws = run_gpu(x, deterministic=(mode == "deterministic"),
+                          fused_cast=(mode == "fused_cast"))
         got[mode] = gpu_groups(ws, x, seqs, groups)
         del inp, ws
         torch.cuda.empty_cache()
@@ -55,9 +57,10 @@ def _check_every_element(w, seqs, groups, row_chunk=1024):
     for mode, g in got.items():
         _log(f"compare {mode}")
         compare_groups(g, ref, x, seqs, groups, label=f"{mode}:")
-    # dK / dV of the two orientations come from the same arithmetic
-    assert np.array_equal(got["atomic"]["dk"], got["deterministic"]["dk"])
-    assert np.array_equal(got["atomic"]["dv"], got["deterministic"]["dv"])
+    # dK / dV of every variant come from the same arithmetic
+    for mode in ("deterministic", "fused_cast"):
+        assert np.array_equal(got["atomic"]["dk"], got[mode]["dk"])
+        assert np.array_equal(got["atomic"]["dv"], got[mode]["dv"])
 
 
 @pytest.mark.timeout(900)

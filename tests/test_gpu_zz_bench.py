@@ -44,6 +44,10 @@ def test_bench_line_contract(capsys):
     assert d["vs_atomic_path"] == pytest.approx(
         (line["kernels_ms"]["attn_bwd_preprocess"] + line["kernels_ms"]["attn_bwd"]
          + line["kernels_ms"]["attn_bwd_postprocess"]) / d["bwd_ms_path"], rel=2e-3)
+    fc = line["fused_cast"]
+    assert fc["bwd_ms"] == pytest.approx(line["kernels_ms"]["attn_bwd_preprocess"]
+                                         + fc["attn_bwd_fused_cast_ms"], rel=0.2)
+    assert fc["vs_separate_cast"] > 0
     au = line["auto"]
     assert au["mode"] == "deterministic" and au["kv_splits"] == 1 and au["bwd_tflops"] > 0
 
@@ -51,8 +55,8 @@ def test_bench_line_contract(capsys):
 def test_secondary_workloads_report_the_hbm_floor(capsys):
     """A short sweep entry carries the compulsory-traffic floor and its timed
     step count (warm-up for 0.3 s, then about 50 ms of timed steps)."""
-    rc = bench.main(["--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--n", "2048",
-                     "--only-extra", "mha_causal_n4096"])
+    rc = bench.main(["--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--workload",
+                     "mha_causal", "--n", "2048", "--only-extra", "mha_causal_n4096"])
     assert rc == 0
     line = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
     e = line["per_workload"]["mha_causal_n4096"]
