@@ -301,6 +301,9 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
           buf_load16(kr, (r * kv_row + 8 * ch) * 2);
     }
   }
+  // LDS address of the tile buffers (direct-to-LDS copies) and this wave's index, formed once.
+  const uint32_t lds0 = lds_addr(smem);
+  const int wu = uni(w);
   // ---- V (and K for D = 64) of this wave's keys as MFMA B operands ---------
   T8 vreg[kKT][C::VREG];
   T8 kreg[C::KREG ? kKT : 1][C::KREG ? D / 16 : 1];
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
       if (ks < C::VREG)
         vreg[kt][ks] = __builtin_bit_cast(T8, buf_load16(vr, off));
       else
-        lds_dma16(vr, smem + C::V_OFF + ((kt * C::VLDS + ks - C::VREG) * NW + uni(w)) * 1024, off);
+        lds_dma16(vr, lds0 + C::V_OFF + ((kt * C::VLDS + ks - C::VREG) * NW + wu) * 1024, off);
       if constexpr (C::KREG) kreg[kt][ks] = __builtin_bit_cast(T8, buf_load16(kr, off));
     }
   }
@@ -361,23 +364,22 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
       // Rows past the sequence end repeat the last row; P = dS = 0 there
       // whatever Q / dO hold (their lse is stored as +inf, or, when lse is
       // copied raw, the edge-tile pass masks them).
-      const int P0 = uni(64 * (w + NW * u));  // wave-uniform
+      const int P0 = 64 * (wu + NW * u);  // wave-uniform
       const int P = P0 + lane;
       const int r = P / C::CH, ch = (P % C::CH) ^ chunk_swz<D>(r);
       const uint32_t off = ((uint32_t)min(r, rows - 1) * q_row + 8 * ch) * 2;
-      const int lds = buf * C::QT + 16 * P0;
-      lds_dma16(qr, smem + C::Q_OFF + lds, off);
-      lds_dma16(dr, smem + C::DO_OFF + lds, off);
+      const uint32_t lds = lds0 + (uint32_t)(buf * C::QT + 16 * P0);
+      lds_dma16(qr, lds + C::Q_OFF, off);
+      lds_dma16(dr, lds + C::DO_OFF, off);
     }
     // lse / Delta of the pair's rows.
     if constexpr (C::LSE_DMA) {
       // Waves 0 and 1 copy 64 floats each (lanes past the rows read out of
       // range); rows past the sequence end are masked in the edge-tile pass.
       const size_t idx = (size_t)h * p.total + a + q0;
-      const int wu = uni(w);
       if (wu < 2)
         lds_dma4(make_rsrc((wu == 0 ? p.lse : p.delta) + idx, rows * 4),
-                 smem + (wu == 0 ? C::LSE_OFF : C::DLT_OFF) + buf * 256, (uint32_t)lane * 4);
+                 lds0 + (wu == 0 ? C::LSE_OFF : C::DLT_OFF) + buf * 256, lane_here() * 4);
     } else {
       // every thread issues the loads (threads past the block read out of
       // range, i.e. zero) so the number of outstanding memory operations is
@@ -736,17 +738,20 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
       // cached Q / dO (measured: +8 % on the long causal problems).
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __syncthreads();  // ... for every thread of the workgroup
+      // The thread index from values the pair loop keeps live anyway (keeping
+      // threadIdx.x live across the loop costs the loop a register).
+      const int ti = (wu << 6) + lane;
       int* count = reinterpret_cast<int*>(smem);  // the pair loop is done with LDS
       int* list = count + 1;
       constexpr int kPer = 8;  // counter atomics in flight per thread
       const int nqb_max = (p.max_seqlen + BM - 1) / BM;
       for (int base = 0; base < npairs; base += kPer * kThreads) {
-        if (tid == 0) *count = 0;
+        if (ti == 0) *count = 0;
         __syncthreads();
         int old[kPer];
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
-          const int i = base + u * kThreads + tid;
+          const int i = base + u * kThreads + ti;
           old[u] = -1;
           if (i < npairs) {
             const int hh = g * G + i / nq, qb = ib0 + i % nq;
@@ -755,7 +760,7 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
         }
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
-          const int i = base + u * kThreads + tid;
+          const int i = base + u * kThreads + ti;
           if (i < npairs && old[u] + 1 == cast_contributors(ib0 + i % nq, L, BM, kBN, p.window))
             list[atomicAdd(count, 1)] = i;
         }
@@ -768,7 +773,7 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
           // that saw every contributor's release.
           constexpr int kTile = BM * (D / 4);
 #pragma unroll 4
-          for (int e = tid; e < ncast * kTile; e += kThreads) {
+          for (int e = ti; e < ncast * kTile; e += kThreads) {
             const int it = list[e / kTile], r = (e % kTile) / (D / 4), c4 = e % (D / 4);
             const int hh = g * G + it / nq, q = (ib0 + it % nq) * BM + r;
             if (q < L) {  // rows past the sequence end of its last block

@@ -154,15 +154,21 @@ __device__ __forceinline__ typename V8<T>::type tr_pair(const char* smem, int of
   return __builtin_bit_cast(typename V8<T>::type, r);
 }
 
+// LDS byte address of a location in a __shared__ array: the value M0 takes
+// for a direct-to-LDS copy.  Formed once per kernel (the conversion from a
+// generic pointer costs a null check and the aperture base in scalar code).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
 // 16 bytes per lane from a buffer straight into LDS: lane l writes bytes
-// [16 l, 16 l + 16) after the wave-uniform LDS address `dst`.  Issued as
-// inline assembly so the compiler's wait-count bookkeeping does not follow
-// it (it would otherwise wait for the load before the next LDS access);
-// the kernel waits for it explicitly before the barrier that publishes it.
-// M0 (which supplies the LDS address) is saved and restored around it.
-__device__ __forceinline__ void lds_dma16(rsrc_t r, char* dst, uint32_t off) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
+// [16 l, 16 l + 16) after the wave-uniform LDS address `lds` (lds_addr plus
+// uniform offsets).  Issued as inline assembly so the compiler's wait-count
+// bookkeeping does not follow it (it would otherwise wait for the load before
+// the next LDS access); the kernel waits for it explicitly before the barrier
+// that publishes it.  M0 (which supplies the LDS address) is saved and
+// restored around it.
+__device__ __forceinline__ void lds_dma16(rsrc_t r, uint32_t lds, uint32_t off) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -171,7 +177,7 @@ __device__ __forceinline__ void lds_dma16(rsrc_t r, char* dst, uint32_t off) {
       "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(base), "v"(off), "s"(r)
+      : "s"(lds), "v"(off), "s"(r)
       : "memory");
 }
 
@@ -180,10 +186,8 @@ __device__ __forceinline__ void lds_dma16(rsrc_t r, char* dst, uint32_t off) {
 // kVmcnt0 + n (n < 16) waits until at most n are outstanding.
 constexpr int kVmcnt0 = 0x0F70;
 
-// Same for 4 bytes per lane: lane l writes bytes [4 l, 4 l + 4) after `dst`.
-__device__ __forceinline__ void lds_dma4(rsrc_t r, char* dst, uint32_t off) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
+// Same for 4 bytes per lane: lane l writes bytes [4 l, 4 l + 4) after `lds`.
+__device__ __forceinline__ void lds_dma4(rsrc_t r, uint32_t lds, uint32_t off) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -192,8 +196,17 @@ __device__ __forceinline__ void lds_dma4(rsrc_t r, char* dst, uint32_t off) {
       "buffer_load_dword %2, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(base), "v"(off), "s"(r)
+      : "s"(lds), "v"(off), "s"(r)
       : "memory");
+}
+
+// This lane's index within the wave, computed where it is used.  The asm is
+// volatile so the value is not hoisted out of a loop and held in a register
+// across it (in register-bound loops the compiler would rather spill it).
+__device__ __forceinline__ uint32_t lane_here() {
+  uint32_t l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
 }
 
 // Wave-uniform integer kept in a scalar register (buffer descriptor fields

@@ -174,23 +174,34 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(DqArgs p) {
     const int r = P / C::CH, ch = (P % C::CH) ^ chunk_swz<D>(r);
     coff[u] = ((uint32_t)r * kv_row + 8 * ch) * 2;
   }
+  // Copy u of a block fills the K tile for u < NDMA / 2 and the V tile
+  // otherwise; its wave-uniform LDS address is this wave's base plus
+  // constants, formed once.
+  const uint32_t lds_w = lds_addr(smem) + 1024u * (uint32_t)uni(w);
   auto issue = [&](int kb, int stage) {
     const int nk = uni(min(L - kb, kDqBN));
     const size_t base = row_off<D, BHSD>(a, kb, g, p.hkv, p.max_seqlen);
     const rsrc_t kr = make_rsrc(kp + base, nk * kv_row * 2);
     const rsrc_t vr = make_rsrc(vp + base, nk * kv_row * 2);
+    const uint32_t lds_s = lds_w + (uint32_t)uni(stage) * C::STAGE;
+    constexpr int kHalf = C::NDMA / 2;
+    if (nk == kDqBN) {
 #pragma unroll
-    for (int u = 0; u < C::NDMA; ++u) {
-      const int P0 = uni(64 * (w + kDqNW * u));
-      const bool isv = P0 >= kDqBN * C::CH;
-      const int Pt = P0 - (isv ? kDqBN * C::CH : 0);  // first chunk of the wave in its tile
-      uint32_t off = coff[u];
-      if (nk < kDqBN) {  // tail block
-        const int P = Pt + lane;
-        const int r = P / C::CH, ch = (P % C::CH) ^ chunk_swz<D>(r);
-        off = ((uint32_t)min(r, nk - 1) * kv_row + 8 * ch) * 2;
+      for (int u = 0; u < C::NDMA; ++u) {
+        const bool isv = u >= kHalf;
+        const int uu = isv ? u - kHalf : u;
+        lds_dma16(isv ? vr : kr, lds_s + (isv ? C::TILE : 0) + 1024u * kDqNW * uu, coff[u]);
       }
-      lds_dma16(isv ? vr : kr, smem + stage * C::STAGE + (isv ? C::TILE : 0) + 16 * Pt, off);
+    } else {  // tail block: rows past the end repeat the last key
+#pragma unroll
+      for (int u = 0; u < C::NDMA; ++u) {
+        const bool isv = u >= kHalf;
+        const int uu = isv ? u - kHalf : u;
+        const int P = 64 * (w + kDqNW * uu) + lane;
+        const int r = P / C::CH, ch = (P % C::CH) ^ chunk_swz<D>(r);
+        const uint32_t off = ((uint32_t)min(r, nk - 1) * kv_row + 8 * ch) * 2;
+        lds_dma16(isv ? vr : kr, lds_s + (isv ? C::TILE : 0) + 1024u * kDqNW * uu, off);
+      }
     }
   };
 

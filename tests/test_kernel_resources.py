@@ -10,9 +10,9 @@ stores to the count and let the barrier publish a tile that has not landed.
 This test compiles bwd.hip to assembly and requires that no scratch
 instruction sits in any loop that issues direct-to-LDS copies, for every
 instantiation; it also bounds the spills the compiler reports per kernel
-(bwd_kernel: at most one VGPR, spilled before and reloaded after its loop in
-some D = 128 variants; the forward and the dQ pass wait for all their copies
-with a zero count, so their spills cannot break a count)."""
+(bwd_kernel: at most two VGPRs, spilled before and reloaded after its loop
+in some D = 128 variants; the forward and the dQ pass wait for all their
+copies with a zero count, so their spills cannot break a count)."""
 import os
 import re
 import shutil
@@ -95,18 +95,18 @@ def test_no_scratch_in_the_copy_pipelined_loops(tmp_path):
     asm, err = _compile_asm(os.path.join(CSRC, "bwd.hip"), tmp_path)
     funcs = {n: f for n, f in _functions(asm).items() if "bwd_kernel" in n}
     assert len(funcs) >= 20, sorted(funcs)
-    pipelined = 0
+    pipelined, bad = 0, []
     for name, lines in funcs.items():
         for head, body in _loops(lines).items():
             text = "\n".join(body)
             if re.search(r"buffer_load_dword\S*\s.*\blds\b", text):
                 pipelined += 1
-                bad = [ln.strip() for ln in body if "scratch_" in ln]
-                assert not bad, f"{name}: scratch access in the copy loop {head}: {bad[:4]}"
+                bad += [(name, head, ln.strip()) for ln in body if "scratch_" in ln]
+    assert not bad, f"scratch access in a copy loop: {bad[:4]}"
     assert pipelined >= len(funcs)  # every instantiation has its pair loop
     rem = _remarks(err)
     for name in funcs:
-        assert rem[name]["vgpr_spill"] <= 1 and rem[name]["scratch"] <= 8, (name, rem[name])
+        assert rem[name]["vgpr_spill"] <= 2 and rem[name]["scratch"] <= 16, (name, rem[name])
 
 
 @pytest.mark.parametrize("src,kernel,max_spill", [("dq.hip", "dq_kernel", 1),
