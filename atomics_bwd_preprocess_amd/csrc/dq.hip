@@ -45,7 +45,10 @@ struct DqCfg {
   static constexpr int BYTES = 2 * STAGE;                     // two stages
   static constexpr int NDMA = 2 * kDqBN * CH / kDqThreads;    // 16-byte copies per thread per block
   static_assert(kDqBN * CH % 64 == 0 && NDMA * kDqThreads == 2 * kDqBN * CH, "copy split");
-  static_assert(2 * BYTES <= 160 * 1024, "two workgroups per CU");
+  // Workgroups per CU: three at D = 64 (about 150 registers per wave), two
+  // at D = 128.
+  static constexpr int WGS = D == 64 ? 3 : 2;
+  static_assert(WGS * BYTES <= 160 * 1024, "LDS for WGS workgroups per CU");
 };
 
 struct DqArgs {
@@ -71,7 +74,7 @@ struct DqArgs {
 // its rows can see (measured 8 % faster at W = 128, 2 % slower on long
 // causal problems, hence only here).
 template <typename T, int D, bool BHSD, bool WIN>
-__global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(DqArgs p) {
+__global__ __launch_bounds__(kDqThreads, DqCfg<D>::WGS) void dq_kernel(DqArgs p) {
   using C = DqCfg<D>;
   using T8 = typename V8<T>::type;
   using T4 = typename V8<T>::half_type;
@@ -236,6 +239,20 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(DqArgs p) {
           const int o = rm_off<D>(32 * mt + n, 16 * ks + 8 * c);
           st = mfma32(lds16<T>(kt, o), qreg[ks], st);
           dpt = mfma32(lds16<T>(vt, o), dreg[ks], dpt);
+        }
+        // D = 64: operand reads run ahead of the products (AHEAD reads first,
+        // then product / read pairs, then the last products) instead of one
+        // product ahead: 4 x 32k 6.45 -> 6.30 ms.  At D = 128 the compiler
+        // then hoists all sixteen reads and spills (slower), so not there.
+        if constexpr (D == 64) {
+          constexpr int AHEAD = 3, NPROD = 2 * (D / 16);
+          __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+          for (int u = 0; u < NPROD - AHEAD; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
         }
         // dS^T = P^T o (dP^T - Delta); register r holds key
         // kb + 32 mt + (r / 4) * 8 + 4 c + r % 4 of query qi.

@@ -39,7 +39,10 @@ struct FwdCfg {
   static constexpr int BYTES = 2 * STAGE;                        // two stages
   static constexpr int NDMA = 2 * kFwdBN * CH / kFwdThreads;     // 16-byte copies per thread per block
   static_assert(kFwdBN * CH % 64 == 0 && NDMA * kFwdThreads == 2 * kFwdBN * CH, "copy split");
-  static_assert(2 * BYTES <= 160 * 1024, "two workgroups per CU");
+  // Workgroups per CU: four at D = 64 (about 120 registers per wave), two at
+  // D = 128.
+  static constexpr int WGS = D == 64 ? 4 : 2;
+  static_assert(WGS * BYTES <= 160 * 1024, "LDS for WGS workgroups per CU");
 };
 
 // acc + the sum of the 8 values, two per v_dot2_f32_{f16,bf16} (products
@@ -82,7 +85,7 @@ struct FwdArgs {
 // windows, where a wave also skips the products of the 32-key halves of a
 // block that none of its rows can see (their scores are -inf, their P zero).
 template <typename T, int D, bool BHSD, bool WIN>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs p) {
+__global__ __launch_bounds__(kFwdThreads, FwdCfg<D>::WGS) void fwd_kernel(FwdArgs p) {
   using C = FwdCfg<D>;
   using T8 = typename V8<T>::type;
   using T4 = typename V8<T>::half_type;
