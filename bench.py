@@ -585,7 +585,13 @@ def main(argv=None) -> int:
                     "ceiling_source": ("measured in this run (microbench/atomic_rate.hip)"
                                        if ceiling else "earlier microbenchmark figure"),
                     "note": "device-scope fp32 atomic adds resolve beyond L2 on this part; "
-                            "their device-wide rate, not the MFMA peak, bounds this kernel"},
+                            "their device-wide rate, not the MFMA peak, bounds this kernel",
+                    # The same kernel built without its dQ product and atomics
+                    # (attn_bwd_dkdv, a library entry point) on the same inputs:
+                    # the share of attn_bwd's time that the dQ product plus its
+                    # atomics cost (an upper bound on the atomic overhead).
+                    "without_dq_product_ms": round(r["dkdv_ms"], 4),
+                    "dq_product_and_atomics_share": round(1.0 - r["dkdv_ms"] / r["bwd_ms"], 4)},
         "wall_ms_per_step": round(r["wall_ms_per_step"], 4),
         "deterministic": deterministic_entry(x, r),
         "fused_cast": fused_cast_entry(x, r),
