@@ -350,9 +350,21 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
   // lse / Delta too at D = 128, through registers otherwise.
   float plse = 0.0f, pdlt = 0.0f;
   int prows = 0;
-  auto load_pair = [&](int i, int buf) {
-    const int h = g * G + i / nq;
-    const int q0 = (ib0 + i % nq) * BM;
+  // Pair i = (query head g G + hi, query block ib0 + qi) with i = hi nq + qi.
+  // The loop steps (hi, qi) instead of dividing (a runtime integer division
+  // costs dozens of scalar instructions, twice per pair).
+  struct PairPos {
+    int hi, qi;
+  };
+  auto step_pos = [&](PairPos& pp) {
+    if (++pp.qi == nq) {
+      pp.qi = 0;
+      ++pp.hi;
+    }
+  };
+  auto load_pair = [&](PairPos pp, int buf) {
+    const int h = g * G + pp.hi;
+    const int q0 = (ib0 + pp.qi) * BM;
     const int rows = uni(min(L - q0, BM));  // >= 1: query blocks start inside the sequence
     const size_t qb = row_off<D, BHSD>(a, q0, h, p.hq, p.max_seqlen);
     const rsrc_t qr = make_rsrc(static_cast<const T*>(p.q) + qb, rows * q_row * 2);
@@ -400,11 +412,17 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
     }
   };
 
+  // Positions of the pair being computed and of the pair two ahead (the one
+  // whose copies go out after this pair's barrier).
+  PairPos cur = {i_lo / nq, i_lo % nq};
+  PairPos ahead = cur;
   if (!SPLIT || np > 0) {  // workgroup-uniform; unsplit blocks always have pairs
-    load_pair(i_lo, 0);
+    load_pair(ahead, 0);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     store_pair(0);
-    if (np > 1) load_pair(i_lo + 1, 1);
+    step_pos(ahead);
+    if (np > 1) load_pair(ahead, 1);
+    step_pos(ahead);
     __syncthreads();
   }
 
@@ -428,11 +446,10 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
     }
   };
 
-  for (int j = 0; j < np; ++j) {
-    const int i = i_lo + j;
+  for (int j = 0; j < np; ++j, step_pos(cur)) {
     const int buf = j & 1;
-    const int h = g * G + i / nq;
-    const int q0 = (ib0 + i % nq) * BM;
+    const int h = g * G + cur.hi;
+    const int q0 = (ib0 + cur.qi) * BM;
     const char* qs = smem + C::Q_OFF + buf * C::QT;
     const char* dos = smem + C::DO_OFF + buf * C::QT;
     char* dss = smem + C::DS_OFF + buf * C::DST;
@@ -632,7 +649,10 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
         __builtin_amdgcn_s_waitcnt(kVmcnt0 + after + 8);
     }
     __syncthreads();
-    if (j + 2 < np) load_pair(i + 2, buf);
+    if (j + 2 < np) {
+      load_pair(ahead, buf);
+      step_pos(ahead);
+    }
 
     if constexpr (DQ) {
       // -- dQ partial = dS K for this wave's two 16 x 16 tiles.  Slot (g, e)
