@@ -209,6 +209,23 @@ __device__ int lpt_item(const BwdArgs& p, int nkb, int r, char* smem) {
   return item;
 }
 
+// Scheduling groups for the S / dP products of one pair (D = 128, dK / dV
+// only): the operand reads of k-step ks + AH (K, Q, dO, and V where that
+// k-step is held in LDS) go out before the two products of k-step ks.
+template <int NKS, int VREG, int AH, int KS = 0>
+__device__ __forceinline__ void sdp_groups() {
+  if constexpr (KS == 0) {
+    constexpr int pre = 3 * AH + (AH > VREG ? AH - VREG : 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, pre, 1);
+  }
+  if constexpr (KS < NKS) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+    if constexpr (KS + AH < NKS)
+      __builtin_amdgcn_sched_group_barrier(0x100, 3 + (KS + AH >= VREG ? 1 : 0), 1);
+    sdp_groups<NKS, VREG, AH, KS + 1>();
+  }
+}
+
 // Key-major dS tile (BM queries per row): 8-byte slot s of row r lives at
 // slot s ^ slot_swz(r).  The 8-byte stores resolve 16 lanes (16 consecutive
 // rows) at a time over 32 banks, so slot_swz is a bijection on the low row
@@ -563,6 +580,7 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
         for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) prod_step(mt, ks);
+        if constexpr (D == 128 && !DQ) sdp_groups<D / 16, C::VREG, 1>();
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -604,18 +622,56 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
       // -- dV += P^T dO, dK += dS^T Q over the BM queries (16 per step).
       // Slot (c, e) of step qs holds query 16 qs + (e / 4) * 8 + 4 c + e % 4,
       // where the C layout of S keeps it; the B operands are read transposed.
+      if constexpr (D == 128 && !DQ) {
+        // The (query step, dim tile) steps' transposed operands are read
+        // kAhead steps before their products, through a ring of kAhead + 1
+        // buffers per tensor; the scheduling groups pin that order (left to
+        // itself the compiler issued each step's reads right before its
+        // products and waited for them there, one LDS round trip per step).
+        // Only in the dK / dV-only pass: with the dQ product's registers
+        // live the ring spills, and that pass is bound by its atomics.
+        constexpr int NS = (BM / 16) * NT, kAhead = 2;
+        T8 pa[BM / 16], sa[BM / 16];
 #pragma unroll
-      for (int qs2 = 0; qs2 < BM / 16; ++qs2) {
-        const int mt = qs2 >> 1, rb = 8 * (qs2 & 1);
-        const T8 pa = pack8<T>(sacc[mt], rb);
-        const T8 sa = pack8<T>(pacc[mt], rb);
-        const int row = 16 * qs2 + 4 * c + (l16 >> 2);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
+        for (int qs2 = 0; qs2 < BM / 16; ++qs2) {
+          pa[qs2] = pack8<T>(sacc[qs2 >> 1], 8 * (qs2 & 1));
+          sa[qs2] = pack8<T>(pacc[qs2 >> 1], 8 * (qs2 & 1));
+        }
+        T8 bo[kAhead + 1], bq[kAhead + 1];
+        auto load_b = [&](int i) {
+          const int qs2 = i / NT, t = i % NT;
+          const int row = 16 * qs2 + 4 * c + (l16 >> 2);
           const int col = 32 * t + 16 * g16 + 4 * (lane & 3);
           const int o0 = rm_off<D>(row, col), o1 = rm_off<D>(row + 8, col);
-          dv[kt][t] = mfma32(pa, tr_pair<T>(dos, o0, o1), dv[kt][t]);
-          dk[kt][t] = mfma32(sa, tr_pair<T>(qs, o0, o1), dk[kt][t]);
+          bo[i % (kAhead + 1)] = tr_pair<T>(dos, o0, o1);
+          bq[i % (kAhead + 1)] = tr_pair<T>(qs, o0, o1);
+        };
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) load_b(i);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * kAhead, 0);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          if (i + kAhead < NS) load_b(i + kAhead);
+          const int qs2 = i / NT, t = i % NT;
+          dv[kt][t] = mfma32(pa[qs2], bo[i % (kAhead + 1)], dv[kt][t]);
+          dk[kt][t] = mfma32(sa[qs2], bq[i % (kAhead + 1)], dk[kt][t]);
+          if (i + kAhead < NS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+      } else {
+#pragma unroll
+        for (int qs2 = 0; qs2 < BM / 16; ++qs2) {
+          const int mt = qs2 >> 1, rb = 8 * (qs2 & 1);
+          const T8 pa = pack8<T>(sacc[mt], rb);
+          const T8 sa = pack8<T>(pacc[mt], rb);
+          const int row = 16 * qs2 + 4 * c + (l16 >> 2);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const int col = 32 * t + 16 * g16 + 4 * (lane & 3);
+            const int o0 = rm_off<D>(row, col), o1 = rm_off<D>(row + 8, col);
+            dv[kt][t] = mfma32(pa, tr_pair<T>(dos, o0, o1), dv[kt][t]);
+            dk[kt][t] = mfma32(sa, tr_pair<T>(qs, o0, o1), dk[kt][t]);
+          }
         }
       }
 

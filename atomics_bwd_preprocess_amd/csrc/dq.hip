@@ -240,12 +240,12 @@ __global__ __launch_bounds__(kDqThreads, DqCfg<D>::WGS) void dq_kernel(DqArgs p)
           st = mfma32(lds16<T>(kt, o), qreg[ks], st);
           dpt = mfma32(lds16<T>(vt, o), dreg[ks], dpt);
         }
-        // D = 64: operand reads run ahead of the products (AHEAD reads first,
-        // then product / read pairs, then the last products) instead of one
-        // product ahead: 4 x 32k 6.45 -> 6.30 ms.  At D = 128 the compiler
-        // then hoists all sixteen reads and spills (slower), so not there.
-        if constexpr (D == 64) {
-          constexpr int AHEAD = 3, NPROD = 2 * (D / 16);
+        // Operand reads run ahead of the products (AHEAD reads first, then
+        // product / read pairs, then the last products) instead of one
+        // product ahead: 4 x 32k 6.45 -> 6.30 ms at D = 64.  At D = 128 only
+        // with windows: without them the read-ahead spills (7-14 registers).
+        if constexpr (D == 64 || WIN) {
+          constexpr int AHEAD = D == 64 ? 3 : 2, NPROD = 2 * (D / 16);
           __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
           for (int u = 0; u < NPROD - AHEAD; ++u) {
@@ -275,14 +275,41 @@ __global__ __launch_bounds__(kDqThreads, DqCfg<D>::WGS) void dq_kernel(DqArgs p)
         // (c, e) of step ks holds key 16 ks + (e / 4) * 8 + 4 c + e % 4 of the
         // half, where the C layout of dP^T keeps it; the transposing read of
         // the row-major K tile delivers K^T in the same order.
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const T8 sb = pack8<T>(dpt, 8 * ks);
-          const int row = 32 * mt + 16 * ks + 4 * c + (l16 >> 2);
-#pragma unroll
-          for (int t = 0; t < D / 32; ++t) {
+        if constexpr (D == 128) {
+          // The transposed K operands are read kAh (key step, dim tile)
+          // steps before their products, through a ring of kAh + 1 buffers;
+          // the scheduling groups pin that order (the compiler otherwise
+          // waited for each step's reads right before its product).
+          constexpr int NS = 2 * (D / 32), kAh = 2;
+          const T8 sbv[2] = {pack8<T>(dpt, 0), pack8<T>(dpt, 8)};
+          T8 ka[kAh + 1];
+          auto load_a = [&](int i) {
+            const int ks = i / (D / 32), t = i % (D / 32);
+            const int row = 32 * mt + 16 * ks + 4 * c + (l16 >> 2);
             const int col = 32 * t + 16 * g16 + 4 * (lane & 3);
-            qacc[t] = mfma32(tr_pair<T>(kt, rm_off<D>(row, col), rm_off<D>(row + 8, col)), sb, qacc[t]);
+            ka[i % (kAh + 1)] = tr_pair<T>(kt, rm_off<D>(row, col), rm_off<D>(row + 8, col));
+          };
+#pragma unroll
+          for (int i = 0; i < kAh; ++i) load_a(i);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAh, 2);
+#pragma unroll
+          for (int i = 0; i < NS; ++i) {
+            if (i + kAh < NS) load_a(i + kAh);
+            const int t = i % (D / 32);
+            qacc[t] = mfma32(ka[i % (kAh + 1)], sbv[i / (D / 32)], qacc[t]);
+            if (i + kAh < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const T8 sb = pack8<T>(dpt, 8 * ks);
+            const int row = 32 * mt + 16 * ks + 4 * c + (l16 >> 2);
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t) {
+              const int col = 32 * t + 16 * g16 + 4 * (lane & 3);
+              qacc[t] = mfma32(tr_pair<T>(kt, rm_off<D>(row, col), rm_off<D>(row + 8, col)), sb, qacc[t]);
+            }
           }
         }
       }
