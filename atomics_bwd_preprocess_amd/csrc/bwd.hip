@@ -10,8 +10,9 @@
 // Work decomposition.  One workgroup (8 waves, two per SIMD) owns one
 // (sequence, kv head g, block of 256 keys); wave w owns keys [32w, 32w + 32)
 // as one 32-key MFMA tile.  The loop runs over every query head of the
-// group and, per head, over every query block that can see the key block
-// under the causal / window masks ("pairs").
+// group and every query block that can see the key block under the causal /
+// window masks ("pairs"): head by head in the atomic pass, query block by
+// query block (from the sequence end) in the passes without dQ atomics.
 //  * dK and dV of the wave's 32 keys accumulate in fp32 registers over the
 //    whole loop -- every query block of every head of the group -- and are
 //    written once at the end, with no atomics (tilelang PR "[GQA] Add
@@ -367,14 +368,26 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
   // lse / Delta too at D = 128, through registers otherwise.
   float plse = 0.0f, pdlt = 0.0f;
   int prows = 0;
-  // Pair i = (query head g G + hi, query block ib0 + qi) with i = hi nq + qi.
+  // Pair i = (query head g G + hi, query block ib0 + qi).  The atomic pass
+  // walks head by head, i = hi nq + qi.  The passes without dQ atomics walk
+  // query blocks from the sequence end down, every head of a block in turn,
+  // i = (nq - 1 - qi) G + hi: all key blocks of a (sequence, kv head) start
+  // at the same query block, and those running on one XCD then read the same
+  // Q / dO tiles at about the same time, so one L2 serves them (in the atomic
+  // pass that order would aim their atomics at the same rows at once).
   // The loop steps (hi, qi) instead of dividing (a runtime integer division
   // costs dozens of scalar instructions, twice per pair).
+  constexpr bool QMAJOR = !DQ;
   struct PairPos {
     int hi, qi;
   };
   auto step_pos = [&](PairPos& pp) {
-    if (++pp.qi == nq) {
+    if constexpr (QMAJOR) {
+      if (++pp.hi == G) {
+        pp.hi = 0;
+        --pp.qi;
+      }
+    } else if (++pp.qi == nq) {
       pp.qi = 0;
       ++pp.hi;
     }
@@ -431,7 +444,7 @@ __global__ __launch_bounds__(64 * nw_of(DQ, SPLIT), 8 / nw_of(DQ, SPLIT)) void b
 
   // Positions of the pair being computed and of the pair two ahead (the one
   // whose copies go out after this pair's barrier).
-  PairPos cur = {i_lo / nq, i_lo % nq};
+  PairPos cur = QMAJOR ? PairPos{i_lo % G, nq - 1 - i_lo / G} : PairPos{i_lo / nq, i_lo % nq};
   PairPos ahead = cur;
   if (!SPLIT || np > 0) {  // workgroup-uniform; unsplit blocks always have pairs
     load_pair(ahead, 0);

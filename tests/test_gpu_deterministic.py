@@ -1,8 +1,9 @@
 """GPU parity of the deterministic backward: the main pass built without its
 dQ product (attn_bwd_dkdv) plus the query-stationary dQ pass (attn_bwd_dq),
 against the fp64 oracle on the same cases as the atomic path, and against the
-atomic path itself: dK / dV bitwise equal, dQ within the tolerance, and every
-output bitwise repeatable run to run."""
+atomic path itself: dK / dV equal within rounding (the same sums, walked query
+block by query block rather than head by head), dQ within the tolerance, and
+every output bitwise repeatable run to run."""
 import numpy as np
 import pytest
 
@@ -55,19 +56,21 @@ def test_against_atomic_path_and_repeatable(w):
     ws_d = path.workspace(inp)
     path.backward(inp, ws_d, o=ws_a.o, lse=ws_a.lse, mode="deterministic")
     torch.cuda.synchronize()
-    # dK / dV come from the same arithmetic in the same order
-    assert torch.equal(ws_d.dk, ws_a.dk) and torch.equal(ws_d.dv, ws_a.dv)
+    # dK / dV: the same products summed in another order -> equal within rounding
+    assert_close(to64(ws_d.dk), to64(ws_a.dk), "dk det vs atomic", w.dtype, atol=1e-3, rtol=1e-2)
+    assert_close(to64(ws_d.dv), to64(ws_a.dv), "dv det vs atomic", w.dtype, atol=1e-3, rtol=1e-2)
     assert torch.equal(ws_d.delta, ws_a.delta)
     if ws_a.dsink is not None:
         assert torch.equal(ws_d.dsink, ws_a.dsink)
     assert_close(to64(ws_d.dq), to64(ws_a.dq), "dq det vs atomic", w.dtype)
-    dq0 = ws_d.dq.clone()
+    dq0, dk0, dv0 = ws_d.dq.clone(), ws_d.dk.clone(), ws_d.dv.clone()
     for _ in range(3):
-        ws_d.dq.zero_()
+        for t in (ws_d.dq, ws_d.dk, ws_d.dv):
+            t.zero_()
         path.backward(inp, ws_d, o=ws_a.o, lse=ws_a.lse, mode="deterministic")
         torch.cuda.synchronize()
         assert torch.equal(ws_d.dq, dq0)
-        assert torch.equal(ws_d.dk, ws_a.dk) and torch.equal(ws_d.dv, ws_a.dv)
+        assert torch.equal(ws_d.dk, dk0) and torch.equal(ws_d.dv, dv0)
 
 
 def test_full_sink_window():

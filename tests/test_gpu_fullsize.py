@@ -57,10 +57,11 @@ def _check_every_element(w, seqs, groups, row_chunk=1024):
     for mode, g in got.items():
         _log(f"compare {mode}")
         compare_groups(g, ref, x, seqs, groups, label=f"{mode}:")
-    # dK / dV of every variant come from the same arithmetic
-    for mode in ("deterministic", "fused_cast"):
-        assert np.array_equal(got["atomic"]["dk"], got[mode]["dk"])
-        assert np.array_equal(got["atomic"]["dv"], got[mode]["dv"])
+    # The fused cast changes nothing in the dK / dV sums: bitwise equal.  The
+    # deterministic pass sums the same products in another order (each was
+    # compared with the oracle above).
+    assert np.array_equal(got["atomic"]["dk"], got["fused_cast"]["dk"])
+    assert np.array_equal(got["atomic"]["dv"], got["fused_cast"]["dv"])
 
 
 @pytest.mark.timeout(900)
