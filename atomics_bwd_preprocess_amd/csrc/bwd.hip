@@ -59,7 +59,7 @@
 // which writes its fp32 dK / dV partial to a workspace slot of its own (no
 // atomics; a reduce pass sums the slots in a fixed order and casts), for
 // problems whose longest key block would otherwise set the critical path.
-// The unsplit dK / dV-only variants run four waves (128 keys) per
+// The dK / dV-only variants (split or not) run four waves (128 keys) per
 // workgroup, two workgroups per CU (see nw_of).
 #include <limits.h>
 
@@ -72,16 +72,18 @@ namespace {
 
 constexpr int kKT = 1;  // 32-key MFMA tiles per wave
 // Waves per workgroup: eight (two per SIMD, one workgroup per CU), except in
-// the unsplit dK / dV-only pass, which runs four, two workgroups per CU.
+// the dK / dV-only passes, which run four, two workgroups per CU.
 // Where only some of a key block's 32-key tiles see a query block (the
 // causal diagonal; under a narrow window about five of eight on every
 // pair), eight waves leave SIMDs idle at the pair's barrier while one SIMD
 // holds two busy waves; two four-wave workgroups share each SIMD without a
 // common barrier, so one fills the other's idle pairs, and short sequences
-// get twice as many workgroups.  The atomic pass keeps 256 keys per
-// workgroup (its atomic bytes scale with 1 / keys per workgroup), and the
-// split pass keeps eight waves as well.
-constexpr int nw_of(bool dq, bool split) { return !dq && !split ? 4 : 8; }
+// get twice as many workgroups; a split part of a 128-key block also holds
+// half the pairs of a 256-key part in about the same time per pair, so
+// splitting shortens the critical path twice as much.  The atomic passes
+// (split or not) keep 256 keys per workgroup: their atomic bytes scale with
+// 1 / keys per workgroup.
+constexpr int nw_of(bool dq, bool /*split*/) { return dq ? 8 : 4; }
 constexpr int kNW = 8;  // the atomic pass
 
 template <int D, int NW = kNW, bool DQ = true>

@@ -132,18 +132,21 @@ def select_mode(shape: Shape, lengths=None) -> str:
     """"deterministic" (query-stationary dQ) or "atomic", whichever measured
     faster on MI355X for this kind of shape, each with its own split choice
     and the deterministic passes ordered by concurrent_dq (whole backward, one
-    MI355X, best split count of each):
-      D = 128: query-stationary faster up to ~1.5k keys per query (GQA 32/8,
-      4 x 1k: 0.19 vs 0.23 ms; 4 x 2k: 0.55 vs 0.60; the ragged varlen batch,
-      ~1.2k keys per query: 1.06 vs 1.13) and with every window measured
-      (W = 128 .. 2048); atomic faster from 2k keys per query (4 x 4k: 1.94
-      vs 2.00 ms; one 8k sequence: 1.81 vs 1.94; 32k: 53.6 vs 59.9);
-      D = 64: atomic faster without a window (4 x 2k: 0.102 vs 0.105 ms,
-      4 x 4k: 0.25 vs 0.31, 4 x 16k: 3.44 vs 4.05); with a window
-      query-stationary is faster up to the largest measured, W = 2048."""
+    MI355X, best of two timings, deterministic / atomic):
+      D = 128: query-stationary faster up to 4k keys per query (GQA 64/8:
+      4 x 2k 1.00 / 1.14 ms, 4 x 4k 3.71 / 3.90, one 8k sequence 3.52 /
+      3.66, 2 x 8k 7.21 / 7.33; GQA 32/8 the same way; the ragged varlen
+      batch, ~1.2k keys per query) and with every window measured
+      (W = 128 .. 2048); level at 8k keys per query (one 16k sequence 14.07 /
+      14.19, 2 x 16k 27.96 / 27.84); atomic faster at 16k (one 32k sequence:
+      55.0 / 54.1);
+      D = 64: atomic faster without a window (4 x 1k: 0.086 / 0.060 ms,
+      4 x 4k: 0.289 / 0.253, 4 x 8k: 1.054 / 0.947; 4 x 2k within 3 %); with
+      a window query-stationary is faster up to the largest measured,
+      W = 2048."""
     kq = keys_per_query(shape, lengths)
     if shape.head_dim == 128:
-        return "deterministic" if (shape.window > 0 or kq <= 1536) else "atomic"
+        return "deterministic" if (shape.window > 0 or kq <= 6144) else "atomic"
     return "deterministic" if 0 < shape.window <= 2048 else "atomic"
 
 
@@ -215,11 +218,12 @@ def concurrent_dq(shape: Shape, lengths=None) -> bool:
 
 def splits_for_mode(shape: Shape, lengths, mode: str) -> int:
     """select_splits for the atomic backward; for the deterministic one,
-    half of it (rounded up), and none below three parts: its unsplit
-    dK / dV-only pass already runs 128-key workgroups, twice as many as the
-    256-key split pass has per part (measured: the varlen batch 1.06 ms
-    unsplit vs 1.16 ms in two parts; GQA 32/8 4 x 1k 0.19 ms in two parts vs
-    0.23 ms in four)."""
+    half of it (rounded up), and none below three parts: its dK / dV-only
+    pass (split or not) runs 128-key workgroups, twice as many as the atomic
+    pass's 256-key ones, and where the atomic pass would split in two the
+    concurrent dQ pass already fills the tail (measured, four-wave split
+    pass: the varlen batch 1.04 ms unsplit vs 1.09 in two parts; GQA 32/8
+    4 x 1k 0.179 ms in two parts vs 0.209 unsplit and 0.191 in four)."""
     n = select_splits(shape, lengths)
     if mode == "deterministic":
         return 1 if n <= 2 else -(-n // 2)

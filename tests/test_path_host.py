@@ -40,7 +40,9 @@ def test_keys_per_query_without_lengths_assumes_a_dense_batch():
     ("mha_causal", dict(n=1024), "atomic"),
     ("long_gqa", {}, "atomic"),                    # D=128, 16k keys per query
     ("varlen_gqa", {}, "deterministic"),           # D=128, ~1.2k keys per query
-    ("varlen_gqa", dict(seqlens=(4096,) * 4, draw_lengths=None), "atomic"),  # 2k keys per query
+    ("varlen_gqa", dict(seqlens=(4096,) * 4, draw_lengths=None), "deterministic"),  # 2k
+    ("long_gqa", dict(seqlens=(8192,), draw_lengths=None), "deterministic"),  # 4k keys per query
+    ("long_gqa", dict(seqlens=(16384, 16384), draw_lengths=None), "atomic"),  # 8k: level
     ("sink_window", {}, "deterministic"),          # D=128, W=128
     ("mha_causal", dict(n=8192, window=128), "deterministic"),
     ("mha_causal", dict(n=8192, window=2048), "deterministic"),
