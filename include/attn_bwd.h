@@ -197,8 +197,11 @@ attn_status_t attn_bwd_fused_cast(const attn_shape_t* shape, const void* q, cons
 
 /*
  * Deterministic backward, pass 1 of 2: the main pass above without its dQ
- * product.  Writes dk and dv exactly as attn_bwd does (bitwise the same
- * values); issues no atomics and needs no dq_accum.
+ * product.  Writes the dk and dv of attn_bwd up to fp32 summation order: it
+ * sums the same products query block by query block from the sequence end
+ * (every head of a block in turn), where attn_bwd goes head by head.  The
+ * result is bitwise reproducible run to run; issues no atomics and needs no
+ * dq_accum.
  */
 attn_status_t attn_bwd_dkdv(const attn_shape_t* shape, const void* q, const void* k,
                             const void* v, const void* dout, const float* lse,
