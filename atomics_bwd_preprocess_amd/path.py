@@ -300,13 +300,12 @@ def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
                             ws.delta, None if det else ws.dq_accum,
                             None if det else ws.dsink, stream)
     if conc:
-        # dQ pass on the side stream, concurrent with the dK / dV pass
-        # (both only read what the preprocess wrote; joined below).
+        # The side stream starts after the preprocess; the dQ pass goes on it
+        # once the dK / dV pass is enqueued (both only read what the
+        # preprocess wrote; joined below).
         main = torch.cuda.current_stream() if stream is None else stream
         side = _side_stream(inp.q.device)
         side.wait_stream(main)
-        attn_bwd_dq(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dq,
-                    side)
     if kv_splits > 1:
         part = _split_workspace(inp, ws, kv_splits)
         attn_bwd_split(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu,
@@ -321,6 +320,12 @@ def backward(inp: Inputs, ws: Workspace, stream=None, o=None, lse=None,
     else:
         attn_bwd(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu,
                  ws.dq_accum, ws.dk, ws.dv, stream)
+    if conc:
+        # Enqueued after the dK / dV pass, whose long key blocks then take the
+        # CUs first (measured: the varlen batch 1.004 -> 0.999 ms, one 8k
+        # GQA 32/8 sequence 1.794 -> 1.751 ms).
+        attn_bwd_dq(inp.shape, inp.q, inp.k, inp.v, inp.do, lse, ws.delta, inp.cu, ws.dq,
+                    side)
     if det and inp.sink is not None:
         attn_bwd_dsink(inp.shape, lse, ws.delta, inp.sink, ws.dsink, stream)
     if conc:
