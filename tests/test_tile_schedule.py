@@ -66,3 +66,50 @@ def test_tile_ranges(bm, causal, w):
                 for i, j in itertools.product(range(q0, min(L, q0 + bm)), keys):
                     if visible(i, j, causal, w):
                         assert lo <= (j - kv0) // 32 < hi, (L, kv0, i, j)
+
+
+def walk(nq, G, i_lo, n, qmajor):
+    """The kernel's pair walk from pair i_lo over n pairs (PairPos and
+    step_pos in csrc/bwd.hip): head by head (qmajor False, the atomic pass) or
+    query block by query block from the last one down, every head of a block
+    in turn (qmajor True, the passes without dQ atomics)."""
+    if qmajor:
+        hi, qi = i_lo % G, nq - 1 - i_lo // G
+    else:
+        hi, qi = i_lo // nq, i_lo % nq
+    out = []
+    for _ in range(n):
+        out.append((hi, qi))
+        if qmajor:
+            hi += 1
+            if hi == G:
+                hi, qi = 0, qi - 1
+        else:
+            qi += 1
+            if qi == nq:
+                qi, hi = 0, hi + 1
+    return out
+
+
+@pytest.mark.parametrize("qmajor", [False, True])
+def test_split_parts_walk_every_pair_once(qmajor):
+    # part p of nsplit walks pairs [p n / nsplit, (p + 1) n / nsplit); together
+    # the parts visit each (head, query block) exactly once, in range, whatever
+    # block a part starts in.
+    for nq, G in itertools.product((1, 2, 3, 7, 33), (1, 2, 4, 8)):
+        npairs = nq * G
+        for nsplit in (1, 2, 3, 5, 16):
+            seen = []
+            for p in range(nsplit):
+                lo, hi_ = p * npairs // nsplit, (p + 1) * npairs // nsplit
+                seen += walk(nq, G, lo, hi_ - lo, qmajor)
+            assert sorted(seen) == sorted(itertools.product(range(G), range(nq)))
+
+
+def test_query_major_walk_starts_at_the_last_block():
+    # every key block of a (sequence, kv head) starts at the same (last) query
+    # block and moves down one block per G pairs
+    nq, G = 5, 4
+    w = walk(nq, G, 0, nq * G, True)
+    assert w[0] == (0, nq - 1) and w[-1] == (G - 1, 0)
+    assert [qi for _, qi in w] == [q for q in range(nq - 1, -1, -1) for _ in range(G)]
