@@ -75,3 +75,45 @@ def test_random_configuration(i):
             b, h, s, dd = got[n].shape
             got[n] = got[n].transpose(0, 2, 1, 3).reshape(b * s, h, dd)
     compare_all(got, orc.forward_backward(x), w.dtype, x)
+
+
+def _case2(i):
+    # A second set: group sizes up to the long-context workload's 8, up to
+    # four key-block parts, "auto" dQ mode and the fused dQ cast.
+    rng = np.random.default_rng(5000 + i)
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    hkv = int(rng.choice([1, 2]))
+    g = int(rng.choice([1, 4, 8]))
+    causal = bool(rng.random() < 0.8)
+    window = int(rng.choice([0, 0, 0, 5, 64, 257])) if causal else 0
+    sink = bool(rng.random() < 0.4)
+    nseq = int(rng.integers(1, 4))
+    lengths = tuple(int(x) for x in rng.integers(0, 700, nseq))
+    if sum(lengths) == 0:
+        lengths = lengths[:-1] + (9,)
+    mode = str(rng.choice(["atomic", "deterministic", "auto"]))
+    splits = int(rng.choice([1, 1, 2, 4]))
+    fused = bool(rng.random() < 0.3)
+    w = ai.workload("varlen_gqa").with_(draw_lengths=None, seqlens=lengths, hq=hkv * g, hkv=hkv,
+                                        d=d, dtype=dtype, causal=causal, window=window, sink=sink)
+    return w, mode, splits, fused
+
+
+@pytest.mark.parametrize("i", list(range(48)))
+def test_random_configuration_wide_groups(i):
+    import torch
+
+    from atomics_bwd_preprocess_amd import path
+
+    w, mode, splits, fused = _case2(i)
+    x = ai.generate(w, 100 + i)
+    print(f"\n[case] random-2 {i}: lengths={w.seqlens} hq={w.hq} hkv={w.hkv} d={w.d} {w.dtype} "
+          f"causal={w.causal} window={w.window} sink={w.sink} {mode} splits={splits} "
+          f"fused_cast={fused}", flush=True)
+    inp = path.to_device(x)
+    ws = path.workspace(inp)
+    path.forward(inp, ws)
+    path.backward(inp, ws, mode=mode, kv_splits=splits, fused_cast=fused)
+    torch.cuda.synchronize()
+    compare_all(outputs(ws), orc.forward_backward(x), w.dtype, x)
