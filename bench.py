@@ -509,7 +509,7 @@ def main(argv=None) -> int:
                          "reference reading for the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); the "
               "path shards by (sequence, kv head) with no collective, so N GPUs would each run "
               "this benchmark on their own share.", file=sys.stderr)
         return 2
