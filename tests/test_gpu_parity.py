@@ -90,6 +90,13 @@ EDGE = [
     ("one_past_tiles", ai.workload("long_gqa").with_(seqlens=(257, 33), hq=8, hkv=2)),
     ("d128_noncausal_sink_bf16", ai.workload("tiny_gqa").with_(seqlens=(97, 160), d=128,
                                                                sink=True, dtype="bf16")),
+    # groups wider than the benchmarked ones, down to a single kv head
+    ("g16_d128_one_kv_head", ai.workload("varlen_gqa").with_(draw_lengths=None,
+                                                             seqlens=(300, 77), hq=16, hkv=1)),
+    ("g64_d64_one_kv_head_sink", ai.workload("mha_causal").with_(seqlens=(150, 40), hq=64,
+                                                                 hkv=1, sink=True)),
+    ("g32_d128_window", ai.workload("sink_window").with_(seqlens=(260,), hq=32, hkv=1,
+                                                         window=50)),
     # more (sequence, key block) items than the in-kernel longest-first ranking
     # takes (520 > 512): the fixed key-block-slowest order
     ("many_short_seqs", ai.workload("varlen_gqa").with_(
@@ -100,6 +107,12 @@ EDGE = [
 @pytest.mark.parametrize("label,w", EDGE, ids=[e[0] for e in EDGE])
 def test_edge_cases(label, w):
     _full_compare(w)
+
+
+@pytest.mark.parametrize("label", ["g16_d128_one_kv_head", "g64_d64_one_kv_head_sink",
+                                   "g32_d128_window"])
+def test_wide_groups_deterministic(label):
+    _full_compare(dict(EDGE)[label], deterministic=True)
 
 
 @pytest.mark.parametrize("sink_value", [12.0, -30.0])
